@@ -1,0 +1,397 @@
+/*
+ * moe_oracle.c -- CPU oracle for the A8W4 fused mixture-of-experts layer.
+ *
+ * TEST INFRASTRUCTURE ONLY.  This file is the slow, plain, FP64 statement of
+ * what the layer computes.  Only the tests, the smoke check and the CPU
+ * baseline leg of the benchmark may load it.  It shares no code, header,
+ * table or constant with the HIP library; the product path never calls it.
+ *
+ * What the layer is (aiter PR 5609, "Add DeepSeek V4.1 Flash TP4 gfx950 MoE
+ * tuning", section Configuration): BF16 output, FP8 activations, MXFP4
+ * weights, per-1x32 scaling, interleaved gate/up, SiLU, and no routing-weight
+ * multiplication in stage one.  What one call contains (aiter PR 5904, "Add
+ * tuned a8w4 fused-MoE configs for DeepSeek V4.1-Flash (TP4 + EP, gfx950)",
+ * section "Fused-MoE kernel, expert-parallel benchmark"): sorting, both
+ * stages and the intermediate quantization.
+ *
+ * Number formats are the ones those names denote:
+ *   E2M1 (MXFP4 element), E8M0 (MX block scale): OCP Microscaling Formats
+ *   (MX) v1.0, element and scale tables.
+ *   E4M3 "FN" (FP8 activations): OCP 8-bit Floating Point v1.0, E4M3 row.
+ *
+ * Readings taken where the pages are silent (each one is listed in the
+ * design notes of the repository):
+ *   - FP8 is E4M3FN (bias 7, largest finite 448, no infinities).
+ *   - Block scale: E = floor(log2(amax)) - 8 (8 is the largest exponent of
+ *     E4M3), clamped to [-127, 127]; amax = 0 gives E = -127.  Elements are
+ *     v * 2^-E rounded to the nearest finite E4M3 value, ties to the even
+ *     code, which saturates magnitudes above 448.  Zero keeps its sign.
+ *   - The requantised intermediate is SiLU(g)*u computed exactly (FP64 here),
+ *     with no BF16 rounding before the requantisation.
+ *   - w13 row 2j is gate j and row 2j+1 is up j; element 2i of a row sits in
+ *     the low nibble of byte i and element 2i+1 in the high nibble.
+ *   - Sorted ids are (k << 24) | t; padding holds the sentinel value M.
+ *     Routes of one expert keep ascending flat index t*topk + k; experts
+ *     are visited in ascending local id; experts with no route get no block.
+ *   - Expert ids outside [expert_offset, expert_offset + E) are skipped.
+ *   - The routing weight multiplies the stage-two result; the top-k sum runs
+ *     in ascending k in FP64 and is rounded once to BF16 (nearest, even).
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+/* ---------------------------------------------------------------- formats */
+
+/* E2M1: sign bit 3, exponent bits 2..1 (bias 1), mantissa bit 0.
+ * Exponent field 0 is subnormal: m * 0.5.  OCP MX v1.0, FP4 E2M1. */
+double oracle_e2m1_value(int code)
+{
+    int s = (code >> 3) & 1, e = (code >> 1) & 3, m = code & 1;
+    double mag = (e == 0) ? 0.5 * m : ldexp(1.0 + 0.5 * m, e - 1);
+    return s ? -mag : mag;
+}
+
+/* E8M0: 2^(u - 127); code 255 is NaN.  OCP MX v1.0, scale format. */
+double oracle_e8m0_value(int code)
+{
+    if (code == 255) return NAN;
+    return ldexp(1.0, code - 127);
+}
+
+/* E4M3FN: sign bit 7, exponent bits 6..3 (bias 7), mantissa bits 2..0.
+ * Exponent 0 is subnormal (m * 2^-9); S.1111.111 is NaN; no infinities.
+ * OCP 8-bit Floating Point v1.0, E4M3. */
+double oracle_e4m3_value(int code)
+{
+    int s = (code >> 7) & 1, e = (code >> 3) & 15, m = code & 7;
+    double mag;
+    if (e == 15 && m == 7) return NAN;
+    if (e == 0) mag = ldexp((double)m, -9);
+    else mag = ldexp(1.0 + m / 8.0, e - 7);
+    return s ? -mag : mag;
+}
+
+/* BF16 bits -> value (the top half of an IEEE binary32). */
+double oracle_bf16_value(uint16_t bits)
+{
+    uint32_t u = (uint32_t)bits << 16;
+    float f;
+    memcpy(&f, &u, 4);
+    return (double)f;
+}
+
+/* Nearest BF16 to x, ties to even, overflow to infinity (IEEE default
+ * rounding applied once to the exact FP64 value). */
+uint16_t oracle_bf16_rne(double x)
+{
+    if (isnan(x)) return 0x7FC0;
+    double ax = fabs(x);
+    const double bf16_max = ldexp(255.0, 120); /* (2 - 2^-7) * 2^127 */
+    uint16_t sign = signbit(x) ? 0x8000 : 0;
+    if (ax == 0.0) return sign;
+    int e;
+    frexp(ax, &e);                 /* ax = f * 2^e, f in [0.5, 1) */
+    int ex = e - 1;                /* floor(log2 ax) */
+    if (ex < -126) ex = -126;      /* subnormal range keeps the 2^-133 step */
+    double quantum = ldexp(1.0, ex - 7);
+    double r = nearbyint(ax / quantum) * quantum;  /* ties to even multiple */
+    /* Overflow: anything that rounds beyond the largest finite value. */
+    if (r > bf16_max) return sign | 0x7F80;
+    float rf = (float)r;           /* exact: r is a BF16 value */
+    uint32_t u;
+    memcpy(&u, &rf, 4);
+    return sign | (uint16_t)(u >> 16);
+}
+
+/* Decode tables filled from the decoders above, so that the dot products
+ * below read a value per code instead of recomputing it.  g_e4m3_pos holds the
+ * 127 non-negative finite E4M3 values; entry c is the value of code c, and the
+ * values increase with the code. */
+static double g_e4m3_pos[127];
+static double g_e4m3_all[256];
+static double g_e2m1_all[16];
+static double g_e8m0_all[256];
+static int g_e4m3_ready = 0;
+
+static void e4m3_table_init(void)
+{
+    if (g_e4m3_ready) return;
+    for (int c = 0; c < 127; ++c) g_e4m3_pos[c] = oracle_e4m3_value(c);
+    for (int c = 0; c < 256; ++c) g_e4m3_all[c] = oracle_e4m3_value(c);
+    for (int c = 0; c < 256; ++c) g_e8m0_all[c] = oracle_e8m0_value(c);
+    for (int c = 0; c < 16; ++c) g_e2m1_all[c] = oracle_e2m1_value(c);
+    g_e4m3_ready = 1;
+}
+
+/* Encode one value: the nearest finite E4M3 value, ties to the even code
+ * (the even mantissa), magnitudes beyond 448 saturating to 448.  The sign is
+ * kept, so -0 and negatives that round to zero give 0x80. */
+int oracle_e4m3_encode(double x)
+{
+    e4m3_table_init();
+    int neg = signbit(x) ? 1 : 0;
+    double a = fabs(x);
+    int code;
+    if (a >= g_e4m3_pos[126]) {
+        code = 126;
+    } else {
+        /* largest lo with table[lo] <= a */
+        int lo = 0, hi = 126;
+        while (hi - lo > 1) {
+            int mid = (lo + hi) / 2;
+            if (g_e4m3_pos[mid] <= a) lo = mid; else hi = mid;
+        }
+        double dlo = a - g_e4m3_pos[lo], dhi = g_e4m3_pos[hi] - a;
+        if (dlo < dhi) code = lo;
+        else if (dhi < dlo) code = hi;
+        else code = (lo % 2 == 0) ? lo : hi;
+    }
+    return neg ? (code | 0x80) : code;
+}
+
+/* Exponent of the per-1x32 scale for a block whose largest magnitude is
+ * amax: floor(log2 amax) - 8, clamped to [-127, 127]; -127 for amax = 0. */
+int oracle_block_exponent(double amax)
+{
+    if (!(amax > 0.0)) return -127;
+    int e;
+    frexp(amax, &e);
+    int E = (e - 1) - 8;
+    if (E < -127) E = -127;
+    if (E > 127) E = 127;
+    return E;
+}
+
+/* Quantise one block of n values (n = 32 on the path) to E4M3 codes plus one
+ * E8M0 scale code.  OCP MX v1.0 conversion with E4M3 elements. */
+void oracle_quant_block(const double* v, int n, uint8_t* q, uint8_t* scale_code)
+{
+    double amax = 0.0;
+    for (int i = 0; i < n; ++i) {
+        double a = fabs(v[i]);
+        if (a > amax) amax = a;
+    }
+    int E = oracle_block_exponent(amax);
+    *scale_code = (uint8_t)(E + 127);
+    for (int i = 0; i < n; ++i) q[i] = (uint8_t)oracle_e4m3_encode(ldexp(v[i], -E));
+}
+
+/* --------------------------------------------------- activation quantiser */
+
+/* hidden BF16 [M, H] -> codes [M, H] and scales [M, H/32], one E8M0 scale
+ * per run of 32 consecutive values along H (the per-1x32 activation scaling
+ * of the Configuration section of aiter PR 5609). */
+void oracle_quant_act(int64_t M, int64_t H, const uint16_t* x, uint8_t* q, uint8_t* s)
+{
+    e4m3_table_init();
+#pragma omp parallel for schedule(static)
+    for (int64_t t = 0; t < M; ++t) {
+        double blk[32];
+        for (int64_t b = 0; b < H / 32; ++b) {
+            for (int i = 0; i < 32; ++i) blk[i] = oracle_bf16_value(x[t * H + b * 32 + i]);
+            oracle_quant_block(blk, 32, q + t * H + b * 32, s + t * (H / 32) + b);
+        }
+    }
+}
+
+/* ------------------------------------------------------------------- sort */
+
+/* Group the local routes by expert into blocks of bm rows.
+ * Writes sorted_ids[0 .. num_padded) and block_expert[0 .. num_padded/bm);
+ * returns num_padded, or -1 if it would exceed capacity. */
+int64_t oracle_sort(int64_t M, int topk, int E, int expert_offset, int bm,
+                    const int32_t* topk_ids, int32_t* sorted_ids,
+                    int32_t* block_expert, int64_t capacity)
+{
+    int64_t R = M * topk;
+    int64_t pos = 0;
+    for (int e = 0; e < E; ++e) {
+        int64_t start = pos;
+        for (int64_t f = 0; f < R; ++f) {
+            int64_t le = (int64_t)topk_ids[f] - expert_offset;
+            if (le != e) continue;
+            if (pos >= capacity) return -1;
+            int64_t t = f / topk, k = f % topk;
+            sorted_ids[pos++] = (int32_t)((k << 24) | t);
+        }
+        int64_t cnt = pos - start;
+        if (cnt == 0) continue;
+        int64_t padded = (cnt + bm - 1) / bm * bm;
+        while (pos < start + padded) {
+            if (pos >= capacity) return -1;
+            sorted_ids[pos++] = (int32_t)M;
+        }
+        for (int64_t b = start / bm; b < (start + padded) / bm; ++b) block_expert[b] = e;
+    }
+    return pos;
+}
+
+/* ------------------------------------------------------- one routed token */
+
+/* Value of element kk of row `row` of an MXFP4 matrix stored as
+ * codes [rows, K/2] (two per byte, low nibble first) and scales [rows, K/32]. */
+static inline double mxfp4_elem(const uint8_t* codes, const uint8_t* scales,
+                                int64_t K, int64_t row, int64_t kk)
+{
+    uint8_t byte = codes[row * (K / 2) + kk / 2];
+    int c = (kk & 1) ? (byte >> 4) : (byte & 15);
+    return g_e2m1_all[c] * g_e8m0_all[scales[row * (K / 32) + kk / 32]];
+}
+
+/* Stage one, activation and intermediate requantisation, and stage two for
+ * one route of token t to local expert e.
+ *   a_q/a_s : the token's quantised activation row (H codes, H/32 scales)
+ *   h       : out, I values of SiLU(gate) * up in FP64 (may be NULL)
+ *   iq, is  : out, the requantised intermediate (I codes, I/32 scales)
+ *   y       : out, H values of the stage-two product in FP64 (may be NULL)
+ */
+void oracle_route(int64_t H, int64_t I,
+                  const uint8_t* a_q, const uint8_t* a_s,
+                  const uint8_t* w13, const uint8_t* w13_s,
+                  const uint8_t* w2, const uint8_t* w2_s,
+                  double* h, uint8_t* iq, uint8_t* is, double* y)
+{
+    e4m3_table_init();
+    double* a = (double*)malloc(sizeof(double) * H);
+    double* hv = (double*)malloc(sizeof(double) * I);
+    double* iv = (double*)malloc(sizeof(double) * I);
+    for (int64_t kk = 0; kk < H; ++kk)
+        a[kk] = g_e4m3_all[a_q[kk]] * g_e8m0_all[a_s[kk / 32]];
+
+    /* stage one: g_j from row 2j, u_j from row 2j+1; SiLU(g) * u */
+    for (int64_t j = 0; j < I; ++j) {
+        double g = 0.0, u = 0.0;
+        for (int64_t kk = 0; kk < H; ++kk) {
+            g += a[kk] * mxfp4_elem(w13, w13_s, H, 2 * j, kk);
+            u += a[kk] * mxfp4_elem(w13, w13_s, H, 2 * j + 1, kk);
+        }
+        hv[j] = g / (1.0 + exp(-g)) * u;
+    }
+    if (h) memcpy(h, hv, sizeof(double) * I);
+
+    /* intermediate quantisation, per 1x32 along j */
+    for (int64_t c = 0; c < I / 32; ++c) oracle_quant_block(hv + 32 * c, 32, iq + 32 * c, is + c);
+    for (int64_t j = 0; j < I; ++j)
+        iv[j] = g_e4m3_all[iq[j]] * g_e8m0_all[is[j / 32]];
+
+    /* stage two: y_h = sum_j inter_j * w2[h, j] */
+    if (y) {
+        for (int64_t hh = 0; hh < H; ++hh) {
+            double acc = 0.0;
+            for (int64_t j = 0; j < I; ++j) acc += iv[j] * mxfp4_elem(w2, w2_s, I, hh, j);
+            y[hh] = acc;
+        }
+    }
+    free(a);
+    free(hv);
+    free(iv);
+}
+
+/* ------------------------------------------------------------ whole layer */
+
+/* The layer's output for a list of tokens.
+ *   hidden      BF16 [M, H]; topk_ids i32 [M, topk]; topk_weights f32 [M, topk]
+ *   w13 [E, 2I, H/2], w13_s [E, 2I, H/32], w2 [E, H, I/2], w2_s [E, H, I/32]
+ *   tokens      the ntok token indices to evaluate (NULL = all M in order)
+ *   out_f64     [ntok, H] the FP64 combine before rounding (may be NULL)
+ *   out_bf16    [ntok, H] the BF16 output
+ * A token with no local route gives a row of +0. */
+void oracle_forward(int64_t M, int64_t H, int64_t I, int E, int expert_offset, int topk,
+                    const uint16_t* hidden, const int32_t* topk_ids, const float* topk_weights,
+                    const uint8_t* w13, const uint8_t* w13_s,
+                    const uint8_t* w2, const uint8_t* w2_s,
+                    const int64_t* tokens, int64_t ntok,
+                    double* out_f64, uint16_t* out_bf16)
+{
+    e4m3_table_init();
+    if (!tokens) ntok = M;
+    int64_t nroute = ntok * topk;
+    /* y for every (listed token, slot); computed in parallel over routes */
+    double* y = (double*)calloc((size_t)(nroute > 0 ? nroute : 1) * H, sizeof(double));
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t r = 0; r < nroute; ++r) {
+        int64_t i = r / topk, k = r % topk;
+        int64_t t = tokens ? tokens[i] : i;
+        int64_t le = (int64_t)topk_ids[t * topk + k] - expert_offset;
+        if (le < 0 || le >= E) continue;
+        uint8_t* aq = (uint8_t*)malloc(H);
+        uint8_t* as = (uint8_t*)malloc(H / 32);
+        uint8_t* iq = (uint8_t*)malloc(I);
+        uint8_t* is = (uint8_t*)malloc(I / 32);
+        double blk[32];
+        for (int64_t b = 0; b < H / 32; ++b) {
+            for (int q = 0; q < 32; ++q) blk[q] = oracle_bf16_value(hidden[t * H + b * 32 + q]);
+            oracle_quant_block(blk, 32, aq + b * 32, as + b);
+        }
+        oracle_route(H, I, aq, as,
+                     w13 + le * (2 * I) * (H / 2), w13_s + le * (2 * I) * (H / 32),
+                     w2 + le * H * (I / 2), w2_s + le * H * (I / 32),
+                     NULL, iq, is, y + r * H);
+        free(aq); free(as); free(iq); free(is);
+    }
+    /* combine: sum over local slots in ascending k, weight applied here */
+#pragma omp parallel for schedule(static)
+    for (int64_t i = 0; i < ntok; ++i) {
+        int64_t t = tokens ? tokens[i] : i;
+        for (int64_t hh = 0; hh < H; ++hh) {
+            double o = 0.0;
+            for (int k = 0; k < topk; ++k) {
+                int64_t le = (int64_t)topk_ids[t * topk + k] - expert_offset;
+                if (le < 0 || le >= E) continue;
+                o += (double)topk_weights[t * topk + k] * y[(i * topk + k) * H + hh];
+            }
+            if (out_f64) out_f64[i * H + hh] = o;
+            out_bf16[i * H + hh] = oracle_bf16_rne(o);
+        }
+    }
+    free(y);
+}
+
+/* The requantised intermediate of a list of routes (flat index f = t*topk+k),
+ * for comparison with the stage-one output.  Routes that are not local give
+ * all-zero rows.  h_f64 [nr, I] may be NULL. */
+void oracle_intermediate(int64_t M, int64_t H, int64_t I, int E, int expert_offset, int topk,
+                         const uint16_t* hidden, const int32_t* topk_ids,
+                         const uint8_t* w13, const uint8_t* w13_s,
+                         const int64_t* routes, int64_t nr,
+                         double* h_f64, uint8_t* iq, uint8_t* is)
+{
+    e4m3_table_init();
+    (void)M;
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t r = 0; r < nr; ++r) {
+        int64_t f = routes[r], t = f / topk;
+        int64_t le = (int64_t)topk_ids[f] - expert_offset;
+        memset(iq + r * I, 0, I);
+        memset(is + r * (I / 32), 0, I / 32);
+        if (h_f64) memset(h_f64 + r * I, 0, sizeof(double) * I);
+        if (le < 0 || le >= E) continue;
+        uint8_t* aq = (uint8_t*)malloc(H);
+        uint8_t* as = (uint8_t*)malloc(H / 32);
+        double blk[32];
+        for (int64_t b = 0; b < H / 32; ++b) {
+            for (int q = 0; q < 32; ++q) blk[q] = oracle_bf16_value(hidden[t * H + b * 32 + q]);
+            oracle_quant_block(blk, 32, aq + b * 32, as + b);
+        }
+        oracle_route(H, I, aq, as,
+                     w13 + le * (2 * I) * (H / 2), w13_s + le * (2 * I) * (H / 32),
+                     NULL, NULL,
+                     h_f64 ? h_f64 + r * I : NULL, iq + r * I, is + r * (I / 32), NULL);
+        free(aq); free(as);
+    }
+}
+
+int oracle_num_threads(void)
+{
+#ifdef _OPENMP
+    return omp_get_max_threads();
+#else
+    return 1;
+#endif
+}
