@@ -1,0 +1,158 @@
+/*
+ * moe_a8w4.h -- C ABI of the A8W4 fused mixture-of-experts layer for MI355X
+ * (gfx950): FP8 E4M3 activations with per-1x32 E8M0 scales times MXFP4
+ * (E2M1 + E8M0 per 1x32) expert weights, BF16 output.
+ *
+ * What one call computes is the layer of aiter PR 5609 ("Add DeepSeek V4.1
+ * Flash TP4 gfx950 MoE tuning", section Configuration): BF16 output, FP8
+ * activations, MXFP4 weights, per-1x32 scaling, interleaved gate/up, SiLU,
+ * routing weight applied in stage two only; and it contains what the timed
+ * call of aiter PR 5904 ("Add tuned a8w4 fused-MoE configs for
+ * DeepSeek V4.1-Flash (TP4 + EP, gfx950)", section "Fused-MoE kernel,
+ * expert-parallel benchmark") contains: sorting, both stages and the
+ * intermediate quantization.
+ *
+ *   a_q, a_s  = per-1x32 quantisation of hidden (E8M0 exponent
+ *               floor(log2 amax) - 8, clamped at -127; E4M3 elements rounded
+ *               to nearest even, saturating at 448)
+ *   for every route (t, k) whose expert g = topk_ids[t,k] is local,
+ *   e = g - expert_offset in [0, E):
+ *     gate_j = <a_t, w13[e, 2j]>, up_j = <a_t, w13[e, 2j+1]>   (j < I)
+ *     h      = per-1x32 quantisation of SiLU(gate) * up
+ *     y      = w2[e] h                                          (H values)
+ *   out[t] = BF16( sum over local k of topk_weights[t,k] * y_(t,k) )
+ *   Routes of non-local experts contribute nothing; a token with none gets 0.
+ *
+ * Conventions
+ *   - All data pointers are DEVICE pointers owned by the caller.  The library
+ *     allocates nothing, keeps no state between calls and never synchronises:
+ *     every entry point only enqueues work on `stream` and returns.  Buffers
+ *     must stay alive until that work completes.  Inputs are never written.
+ *   - Return value: 0 on success; a negative MOE_ERR_* if the arguments are
+ *     invalid, in which case nothing was enqueued; a positive hipError_t if a
+ *     launch failed.  Faults inside kernels surface at the caller's next
+ *     synchronisation.  moe_a8w4_status_str() names a code.
+ *   - Every pointer must be 16-byte aligned (the workspace 256-byte aligned).
+ *   - Limits: 0 <= M < 2^24; H a positive multiple of 512; I a positive
+ *     multiple of 128; 1 <= E <= 512; 1 <= topk <= 8.
+ *   - No data-dependent value is read back to the host, so calls can be
+ *     captured in a HIP graph and replayed on changed inputs.
+ */
+#ifndef MOE_A8W4_H
+#define MOE_A8W4_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MOE_OK 0
+#define MOE_ERR_NULL (-1)      /* a required pointer is NULL */
+#define MOE_ERR_DIMS (-2)      /* a dimension is outside the limits above */
+#define MOE_ERR_ALIGN (-3)     /* a pointer is not 16-byte (workspace: 256-byte) aligned */
+#define MOE_ERR_WORKSPACE (-4) /* workspace_bytes smaller than moe_a8w4_workspace_bytes() */
+#define MOE_ERR_BLOCK_M (-5)   /* block_m not one of 16, 32, 64, 128 */
+
+typedef struct moe_a8w4_dims {
+  int32_t tokens;        /* M: token rows in hidden / out / topk_* */
+  int32_t hidden;        /* H: model width */
+  int32_t inter;         /* I: intermediate width as stored (zero-padded columns included) */
+  int32_t num_experts;   /* E: experts held in the weight tensors */
+  int32_t expert_offset; /* global id of weight expert 0 (a rank's local-expert slice) */
+  int32_t topk;          /* slots per token */
+} moe_a8w4_dims;
+
+/* ------------------------------------------------------------------ sizes */
+
+/* Bytes of workspace moe_a8w4_forward needs for these dims (an upper bound
+ * independent of the routing).  Writes *bytes; returns a status. */
+int moe_a8w4_workspace_bytes(const moe_a8w4_dims* dims, size_t* bytes);
+
+/* Rows per sorted block (16, 32, 64 or 128) that moe_a8w4_forward uses for
+ * these dims; a function of M, topk and E only.  Negative status if invalid.
+ * The same block_m is shared by the sort and both stages. */
+int moe_a8w4_block_m(const moe_a8w4_dims* dims);
+
+/* Capacity, in entries, that sorted_ids needs for these dims and block_m:
+ * R + min(E, R) * (block_m - 1) rounded up to block_m, R = M * topk.
+ * block_expert needs capacity / block_m entries.  Negative status if invalid. */
+int64_t moe_a8w4_sort_capacity(const moe_a8w4_dims* dims, int32_t block_m);
+
+/* ---------------------------------------------------------------- weights */
+
+/* Reorder MXFP4 expert weights into the layout the GEMM kernels stream
+ * (a one-time, off-path transform; the packed buffers have the same sizes as
+ * the inputs).  Inputs, row-major, element 2i in the low nibble of byte i:
+ *   w13      [E, 2I, H/2]  E2M1 codes; row 2j = gate of column j, row 2j+1 = up
+ *   w13_s    [E, 2I, H/32] E8M0 scale of each run of 32 elements along H
+ *   w2       [E, H, I/2]   E2M1 codes
+ *   w2_s     [E, H, I/32]  E8M0 scales along I
+ * Outputs: w13_p, w13_s_p, w2_p, w2_s_p of the same byte sizes. */
+int moe_a8w4_pack_weights(const moe_a8w4_dims* dims, const uint8_t* w13, const uint8_t* w13_s,
+                          const uint8_t* w2, const uint8_t* w2_s, uint8_t* w13_p, uint8_t* w13_s_p,
+                          uint8_t* w2_p, uint8_t* w2_s_p, hipStream_t stream);
+
+/* ------------------------------------------------------------- the layer */
+
+/* The whole layer: quantise, sort, stage one, stage two, BF16 output.
+ *   hidden        [M, H] BF16
+ *   topk_ids      [M, topk] int32 global expert ids (any value; non-local skipped)
+ *   topk_weights  [M, topk] float32
+ *   w13_p, w13_s_p, w2_p, w2_s_p   weights packed by moe_a8w4_pack_weights
+ *   out           [M, H] BF16, every element overwritten
+ *   workspace     >= moe_a8w4_workspace_bytes(dims) bytes, contents ignored
+ * M = 0 enqueues nothing and succeeds. */
+int moe_a8w4_forward(const moe_a8w4_dims* dims, const void* hidden, const int32_t* topk_ids,
+                     const float* topk_weights, const uint8_t* w13_p, const uint8_t* w13_s_p,
+                     const uint8_t* w2_p, const uint8_t* w2_s_p, void* out, void* workspace,
+                     size_t workspace_bytes, hipStream_t stream);
+
+/* ----------------------------------------------- the steps, one at a time */
+
+/* Per-1x32 FP8 quantisation of BF16 rows: x [M, H] -> q [M, H] E4M3 codes,
+ * s [M, H/32] E8M0 codes.  If zero_f32 is not NULL, [M, H] floats there are
+ * set to 0 (the combine buffer of stage two).  H must be a multiple of 32. */
+int moe_a8w4_quant_act(int32_t M, int32_t H, const void* x, uint8_t* q, uint8_t* s, float* zero_f32,
+                       hipStream_t stream);
+
+/* Group local routes by expert: sorted_ids [capacity] receives, expert by
+ * expert in ascending local id, the expert's routes in ascending t*topk + k
+ * as (k << 24) | t, each expert's run padded with M to a multiple of block_m
+ * (experts without routes get no rows); block_expert [capacity/block_m]
+ * receives the local expert of each block; num_padded [1] the total rows.
+ * Entries past num_padded are left unspecified. */
+int moe_a8w4_sort(const moe_a8w4_dims* dims, int32_t block_m, const int32_t* topk_ids,
+                  int32_t* sorted_ids, int32_t* block_expert, int32_t* num_padded,
+                  hipStream_t stream);
+
+/* Stage one for every sorted block: inter_q [capacity, I] E4M3 codes and
+ * inter_s [capacity, I/32] E8M0 codes, row p = sorted position, holding the
+ * per-1x32 quantisation of SiLU(gate) * up.  Rows of blocks that hold a
+ * route are written in full (padding columns included); rows past the last
+ * route of a block may be left unwritten. */
+int moe_a8w4_stage1(const moe_a8w4_dims* dims, int32_t block_m, const uint8_t* a_q,
+                    const uint8_t* a_s, const int32_t* sorted_ids, const int32_t* block_expert,
+                    const int32_t* num_padded, const uint8_t* w13_p, const uint8_t* w13_s_p,
+                    uint8_t* inter_q, uint8_t* inter_s, hipStream_t stream);
+
+/* Stage two: adds topk_weights[t,k] * (w2[e] h) of every route into
+ * acc [M, H] float32 (which must hold zeros, or a partial sum, beforehand). */
+int moe_a8w4_stage2(const moe_a8w4_dims* dims, int32_t block_m, const uint8_t* inter_q,
+                    const uint8_t* inter_s, const int32_t* sorted_ids, const int32_t* block_expert,
+                    const int32_t* num_padded, const float* topk_weights, const uint8_t* w2_p,
+                    const uint8_t* w2_s_p, float* acc, hipStream_t stream);
+
+/* acc [M, H] float32 -> out [M, H] BF16, round to nearest even. */
+int moe_a8w4_finalize(int32_t M, int32_t H, const float* acc, void* out, hipStream_t stream);
+
+/* Name of a status code (static string). */
+const char* moe_a8w4_status_str(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_A8W4_H */

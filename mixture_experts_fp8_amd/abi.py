@@ -1,0 +1,210 @@
+"""Python binding of the C ABI in include/moe_a8w4.h (argument marshalling only).
+
+Every function has the name of the C entry point it calls, takes torch
+tensors that already live on the GPU, and launches on torch's current stream.
+All compute runs in the HIP kernels of libmoe_a8w4.so; if that library is
+missing, loading fails loudly.  There is no CPU fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libmoe_a8w4.so")
+
+MOE_OK = 0
+MOE_ERR_NULL = -1
+MOE_ERR_DIMS = -2
+MOE_ERR_ALIGN = -3
+MOE_ERR_WORKSPACE = -4
+MOE_ERR_BLOCK_M = -5
+
+# every symbol include/moe_a8w4.h declares
+EXPORTS = (
+    "moe_a8w4_workspace_bytes", "moe_a8w4_block_m", "moe_a8w4_sort_capacity",
+    "moe_a8w4_pack_weights", "moe_a8w4_forward", "moe_a8w4_quant_act", "moe_a8w4_sort",
+    "moe_a8w4_stage1", "moe_a8w4_stage2", "moe_a8w4_finalize", "moe_a8w4_status_str",
+)
+
+
+class moe_a8w4_dims(ctypes.Structure):
+    _fields_ = [("tokens", ctypes.c_int32), ("hidden", ctypes.c_int32), ("inter", ctypes.c_int32),
+                ("num_experts", ctypes.c_int32), ("expert_offset", ctypes.c_int32),
+                ("topk", ctypes.c_int32)]
+
+
+def make_dims(tokens, hidden, inter, num_experts, topk, expert_offset=0) -> moe_a8w4_dims:
+    return moe_a8w4_dims(tokens, hidden, inter, num_experts, expert_offset, topk)
+
+
+class MoeError(RuntimeError):
+    def __init__(self, name, status):
+        super().__init__("%s failed: status %d (%s)" % (name, status, status_str(status)))
+        self.status = status
+
+
+_lib = None
+
+
+def load() -> ctypes.CDLL:
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError("HIP library %s is not built; run __graft_entry__.build()" % LIB_PATH)
+    lib = ctypes.CDLL(LIB_PATH)
+    P = ctypes.POINTER(moe_a8w4_dims)
+    vp, i32, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_size_t
+    sig = {
+        "moe_a8w4_workspace_bytes": (ctypes.c_int, [P, ctypes.POINTER(sz)]),
+        "moe_a8w4_block_m": (ctypes.c_int, [P]),
+        "moe_a8w4_sort_capacity": (ctypes.c_int64, [P, i32]),
+        "moe_a8w4_pack_weights": (ctypes.c_int, [P] + [vp] * 8 + [vp]),
+        "moe_a8w4_forward": (ctypes.c_int, [P] + [vp] * 9 + [sz, vp]),
+        "moe_a8w4_quant_act": (ctypes.c_int, [i32, i32, vp, vp, vp, vp, vp]),
+        "moe_a8w4_sort": (ctypes.c_int, [P, i32, vp, vp, vp, vp, vp]),
+        "moe_a8w4_stage1": (ctypes.c_int, [P, i32] + [vp] * 9 + [vp]),
+        "moe_a8w4_stage2": (ctypes.c_int, [P, i32] + [vp] * 9 + [vp]),
+        "moe_a8w4_finalize": (ctypes.c_int, [i32, i32, vp, vp, vp]),
+        "moe_a8w4_status_str": (ctypes.c_char_p, [ctypes.c_int]),
+    }
+    for name, (res, args) in sig.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    _lib = lib
+    return lib
+
+
+def status_str(status: int) -> str:
+    return load().moe_a8w4_status_str(int(status)).decode()
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream=None):
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _check(name, st):
+    if st != MOE_OK:
+        raise MoeError(name, st)
+
+
+# ------------------------------------------------------------------ sizes
+
+def moe_a8w4_workspace_bytes(dims: moe_a8w4_dims) -> int:
+    n = ctypes.c_size_t(0)
+    _check("moe_a8w4_workspace_bytes", load().moe_a8w4_workspace_bytes(ctypes.byref(dims), ctypes.byref(n)))
+    return n.value
+
+
+def moe_a8w4_block_m(dims: moe_a8w4_dims) -> int:
+    bm = load().moe_a8w4_block_m(ctypes.byref(dims))
+    if bm < 0:
+        raise MoeError("moe_a8w4_block_m", bm)
+    return bm
+
+
+def moe_a8w4_sort_capacity(dims: moe_a8w4_dims, block_m: int) -> int:
+    c = load().moe_a8w4_sort_capacity(ctypes.byref(dims), block_m)
+    if c < 0:
+        raise MoeError("moe_a8w4_sort_capacity", c)
+    return c
+
+
+# ---------------------------------------------------------------- weights
+
+def moe_a8w4_pack_weights(dims, w13, w13_s, w2, w2_s, out=None, stream=None):
+    """Packed copies (w13_p, w13_s_p, w2_p, w2_s_p) of uint8 device tensors."""
+    if out is None:
+        out = tuple(torch.empty_like(t) for t in (w13, w13_s, w2, w2_s))
+    st = load().moe_a8w4_pack_weights(ctypes.byref(dims), _ptr(w13), _ptr(w13_s), _ptr(w2), _ptr(w2_s),
+                                      *[_ptr(t) for t in out], _stream(stream))
+    _check("moe_a8w4_pack_weights", st)
+    return out
+
+
+# -------------------------------------------------------------- the layer
+
+def moe_a8w4_forward(dims, hidden, topk_ids, topk_weights, w13_p, w13_s_p, w2_p, w2_s_p,
+                     out=None, workspace=None, stream=None):
+    """BF16 output [M, H] of the layer (out and workspace are allocated if not given)."""
+    if out is None:
+        out = torch.empty((dims.tokens, dims.hidden), dtype=torch.bfloat16, device=hidden.device)
+    if workspace is None:
+        workspace = torch.empty(moe_a8w4_workspace_bytes(dims), dtype=torch.uint8, device=hidden.device)
+    st = load().moe_a8w4_forward(ctypes.byref(dims), _ptr(hidden), _ptr(topk_ids), _ptr(topk_weights),
+                                 _ptr(w13_p), _ptr(w13_s_p), _ptr(w2_p), _ptr(w2_s_p), _ptr(out),
+                                 _ptr(workspace), workspace.numel(), _stream(stream))
+    _check("moe_a8w4_forward", st)
+    return out
+
+
+# ------------------------------------------------------------- the steps
+
+def moe_a8w4_quant_act(x, q=None, s=None, zero_f32=None, stream=None):
+    M, H = x.shape
+    if q is None:
+        q = torch.empty((M, H), dtype=torch.uint8, device=x.device)
+    if s is None:
+        s = torch.empty((M, H // 32), dtype=torch.uint8, device=x.device)
+    st = load().moe_a8w4_quant_act(M, H, _ptr(x), _ptr(q), _ptr(s), _ptr(zero_f32), _stream(stream))
+    _check("moe_a8w4_quant_act", st)
+    return q, s
+
+
+def moe_a8w4_sort(dims, block_m, topk_ids, sorted_ids=None, block_expert=None, num_padded=None,
+                  stream=None):
+    cap = moe_a8w4_sort_capacity(dims, block_m)
+    dev = topk_ids.device
+    if sorted_ids is None:
+        sorted_ids = torch.empty(max(cap, 1), dtype=torch.int32, device=dev)
+    if block_expert is None:
+        block_expert = torch.empty(max(cap // block_m, 1), dtype=torch.int32, device=dev)
+    if num_padded is None:
+        num_padded = torch.empty(1, dtype=torch.int32, device=dev)
+    st = load().moe_a8w4_sort(ctypes.byref(dims), block_m, _ptr(topk_ids), _ptr(sorted_ids),
+                              _ptr(block_expert), _ptr(num_padded), _stream(stream))
+    _check("moe_a8w4_sort", st)
+    return sorted_ids, block_expert, num_padded
+
+
+def moe_a8w4_stage1(dims, block_m, a_q, a_s, sorted_ids, block_expert, num_padded, w13_p, w13_s_p,
+                    inter_q=None, inter_s=None, stream=None):
+    cap = moe_a8w4_sort_capacity(dims, block_m)
+    dev = a_q.device
+    if inter_q is None:
+        inter_q = torch.empty((cap, dims.inter), dtype=torch.uint8, device=dev)
+    if inter_s is None:
+        inter_s = torch.empty((cap, dims.inter // 32), dtype=torch.uint8, device=dev)
+    st = load().moe_a8w4_stage1(ctypes.byref(dims), block_m, _ptr(a_q), _ptr(a_s), _ptr(sorted_ids),
+                                _ptr(block_expert), _ptr(num_padded), _ptr(w13_p), _ptr(w13_s_p),
+                                _ptr(inter_q), _ptr(inter_s), _stream(stream))
+    _check("moe_a8w4_stage1", st)
+    return inter_q, inter_s
+
+
+def moe_a8w4_stage2(dims, block_m, inter_q, inter_s, sorted_ids, block_expert, num_padded,
+                    topk_weights, w2_p, w2_s_p, acc, stream=None):
+    st = load().moe_a8w4_stage2(ctypes.byref(dims), block_m, _ptr(inter_q), _ptr(inter_s),
+                                _ptr(sorted_ids), _ptr(block_expert), _ptr(num_padded),
+                                _ptr(topk_weights), _ptr(w2_p), _ptr(w2_s_p), _ptr(acc),
+                                _stream(stream))
+    _check("moe_a8w4_stage2", st)
+    return acc
+
+
+def moe_a8w4_finalize(acc, out=None, stream=None):
+    M, H = acc.shape
+    if out is None:
+        out = torch.empty((M, H), dtype=torch.bfloat16, device=acc.device)
+    st = load().moe_a8w4_finalize(M, H, _ptr(acc), _ptr(out), _stream(stream))
+    _check("moe_a8w4_finalize", st)
+    return out

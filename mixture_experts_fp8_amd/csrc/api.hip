@@ -1,0 +1,261 @@
+// C ABI of the A8W4 MoE library: argument checks, block size choice,
+// workspace carving and the launch sequence.  Declarations and the contract
+// of every entry point are in include/moe_a8w4.h.
+#include <stdint.h>
+#include <stddef.h>
+
+#include "moe_a8w4.h"
+#include "common.hpp"
+#include "launch.hpp"
+
+namespace {
+
+using moe::GemmArgs;
+
+int check_dims(const moe_a8w4_dims* d) {
+  if (!d) return MOE_ERR_NULL;
+  if (d->tokens < 0 || d->tokens >= (1 << 24)) return MOE_ERR_DIMS;
+  if (d->hidden <= 0 || d->hidden % 512 != 0 || d->hidden > (1 << 20)) return MOE_ERR_DIMS;
+  if (d->inter <= 0 || d->inter % 128 != 0 || d->inter > (1 << 20)) return MOE_ERR_DIMS;
+  if (d->num_experts < 1 || d->num_experts > moe::kMaxExperts) return MOE_ERR_DIMS;
+  if (d->topk < 1 || d->topk > moe::kMaxTopk) return MOE_ERR_DIMS;
+  return MOE_OK;
+}
+
+bool aligned(const void* p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
+
+int status_of(hipError_t e) { return e == hipSuccess ? MOE_OK : (int)e; }
+
+bool valid_bm(int bm) { return bm == 16 || bm == 32 || bm == 64 || bm == 128; }
+
+// Rows per sorted block from the mean number of routes per expert.  Column
+// groups of 16 past a block's last route are skipped by the GEMMs, so a larger
+// block only costs padding; a smaller one re-reads an expert's weights once
+// per extra block.
+int choose_bm(const moe_a8w4_dims* d) {
+  const double avg = (double)d->tokens * d->topk / d->num_experts;
+  if (avg <= 8.0) return 16;
+  if (avg <= 24.0) return 32;
+  if (avg <= 48.0) return 64;
+  return 128;
+}
+
+int64_t capacity(const moe_a8w4_dims* d, int bm) {
+  const int64_t R = (int64_t)d->tokens * d->topk;
+  const int64_t nexp = R < d->num_experts ? R : d->num_experts;
+  const int64_t cap = R + nexp * (bm - 1);
+  return (cap + bm - 1) / bm * bm;
+}
+
+struct Layout {
+  size_t aq, as, sorted, bexp, npad, iq, is, acc, total;
+};
+
+size_t al256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+Layout layout(const moe_a8w4_dims* d, int bm) {
+  const size_t M = d->tokens, H = d->hidden, I = d->inter;
+  const size_t cap = (size_t)capacity(d, bm);
+  Layout L;
+  size_t o = 0;
+  L.aq = o;     o += al256(M * H);
+  L.as = o;     o += al256(M * H / 32);
+  L.sorted = o; o += al256(cap * 4);
+  L.bexp = o;   o += al256(cap / bm * 4);
+  L.npad = o;   o += 256;
+  L.iq = o;     o += al256(cap * I);
+  L.is = o;     o += al256(cap * I / 32);
+  L.acc = o;    o += al256(M * H * 4);
+  L.total = o;
+  return L;
+}
+
+GemmArgs stage1_args(const moe_a8w4_dims* d, int bm, const uint8_t* a_q, const uint8_t* a_s,
+                     const int32_t* sorted, const int32_t* bexp, const int32_t* npad,
+                     const uint8_t* w, const uint8_t* ws, uint8_t* iq, uint8_t* is) {
+  GemmArgs a = {};
+  a.M = d->tokens; a.topk = d->topk; a.N = 2 * d->inter; a.K = d->hidden; a.bm = bm;
+  a.sorted_ids = sorted; a.block_expert = bexp; a.num_padded = npad;
+  a.bq = a_q; a.bs = a_s; a.w = w; a.ws = ws; a.out_q = iq; a.out_s = is;
+  return a;
+}
+
+GemmArgs stage2_args(const moe_a8w4_dims* d, int bm, const uint8_t* iq, const uint8_t* is,
+                     const int32_t* sorted, const int32_t* bexp, const int32_t* npad,
+                     const float* wts, const uint8_t* w, const uint8_t* ws, float* acc) {
+  GemmArgs a = {};
+  a.M = d->tokens; a.topk = d->topk; a.N = d->hidden; a.K = d->inter; a.bm = bm;
+  a.sorted_ids = sorted; a.block_expert = bexp; a.num_padded = npad;
+  a.bq = iq; a.bs = is; a.w = w; a.ws = ws; a.topk_weights = wts; a.acc = acc;
+  return a;
+}
+
+}  // namespace
+
+extern "C" {
+
+int moe_a8w4_workspace_bytes(const moe_a8w4_dims* dims, size_t* bytes) {
+  int st = check_dims(dims);
+  if (st) return st;
+  if (!bytes) return MOE_ERR_NULL;
+  *bytes = layout(dims, choose_bm(dims)).total;
+  return MOE_OK;
+}
+
+int moe_a8w4_block_m(const moe_a8w4_dims* dims) {
+  int st = check_dims(dims);
+  if (st) return st;
+  return choose_bm(dims);
+}
+
+int64_t moe_a8w4_sort_capacity(const moe_a8w4_dims* dims, int32_t block_m) {
+  int st = check_dims(dims);
+  if (st) return st;
+  if (!valid_bm(block_m)) return MOE_ERR_BLOCK_M;
+  return capacity(dims, block_m);
+}
+
+int moe_a8w4_pack_weights(const moe_a8w4_dims* dims, const uint8_t* w13, const uint8_t* w13_s,
+                          const uint8_t* w2, const uint8_t* w2_s, uint8_t* w13_p, uint8_t* w13_s_p,
+                          uint8_t* w2_p, uint8_t* w2_s_p, hipStream_t stream) {
+  int st = check_dims(dims);
+  if (st) return st;
+  const void* ptrs[8] = {w13, w13_s, w2, w2_s, w13_p, w13_s_p, w2_p, w2_s_p};
+  for (const void* p : ptrs) {
+    if (!p) return MOE_ERR_NULL;
+    if (!aligned(p, 16)) return MOE_ERR_ALIGN;
+  }
+  const int64_t E = dims->num_experts, H = dims->hidden, I = dims->inter;
+  hipError_t e = moe::launch_pack(w13, w13_s, w13_p, w13_s_p, E, 2 * I, H, stream);
+  if (e != hipSuccess) return status_of(e);
+  return status_of(moe::launch_pack(w2, w2_s, w2_p, w2_s_p, E, H, I, stream));
+}
+
+int moe_a8w4_forward(const moe_a8w4_dims* dims, const void* hidden, const int32_t* topk_ids,
+                     const float* topk_weights, const uint8_t* w13_p, const uint8_t* w13_s_p,
+                     const uint8_t* w2_p, const uint8_t* w2_s_p, void* out, void* workspace,
+                     size_t workspace_bytes, hipStream_t stream) {
+  int st = check_dims(dims);
+  if (st) return st;
+  if (dims->tokens == 0) return MOE_OK;
+  const void* ptrs[9] = {hidden, topk_ids, topk_weights, w13_p, w13_s_p, w2_p, w2_s_p, out, workspace};
+  for (const void* p : ptrs) {
+    if (!p) return MOE_ERR_NULL;
+    if (!aligned(p, 16)) return MOE_ERR_ALIGN;
+  }
+  if (!aligned(workspace, 256)) return MOE_ERR_ALIGN;
+  const int bm = choose_bm(dims);
+  const Layout L = layout(dims, bm);
+  if (workspace_bytes < L.total) return MOE_ERR_WORKSPACE;
+
+  uint8_t* ws = static_cast<uint8_t*>(workspace);
+  uint8_t* a_q = ws + L.aq;
+  uint8_t* a_s = ws + L.as;
+  int32_t* sorted = reinterpret_cast<int32_t*>(ws + L.sorted);
+  int32_t* bexp = reinterpret_cast<int32_t*>(ws + L.bexp);
+  int32_t* npad = reinterpret_cast<int32_t*>(ws + L.npad);
+  uint8_t* iq = ws + L.iq;
+  uint8_t* is = ws + L.is;
+  float* acc = reinterpret_cast<float*>(ws + L.acc);
+  const int64_t max_blocks = capacity(dims, bm) / bm;
+
+  hipError_t e = moe::launch_act_quant(dims->tokens, dims->hidden,
+                                       static_cast<const uint16_t*>(hidden), a_q, a_s, acc, stream);
+  if (e != hipSuccess) return status_of(e);
+  e = moe::launch_sort(topk_ids, dims->tokens, dims->topk, dims->num_experts, dims->expert_offset,
+                       bm, sorted, bexp, npad, stream);
+  if (e != hipSuccess) return status_of(e);
+  e = moe::launch_stage1(stage1_args(dims, bm, a_q, a_s, sorted, bexp, npad, w13_p, w13_s_p, iq, is),
+                         max_blocks, stream);
+  if (e != hipSuccess) return status_of(e);
+  e = moe::launch_stage2(stage2_args(dims, bm, iq, is, sorted, bexp, npad, topk_weights, w2_p,
+                                     w2_s_p, acc), max_blocks, stream);
+  if (e != hipSuccess) return status_of(e);
+  return status_of(moe::launch_finalize(dims->tokens, dims->hidden, acc,
+                                        static_cast<uint16_t*>(out), stream));
+}
+
+int moe_a8w4_quant_act(int32_t M, int32_t H, const void* x, uint8_t* q, uint8_t* s, float* zero_f32,
+                       hipStream_t stream) {
+  if (M < 0 || H <= 0 || H % 32 != 0) return MOE_ERR_DIMS;
+  if (M == 0) return MOE_OK;
+  if (!x || !q || !s) return MOE_ERR_NULL;
+  if (!aligned(x, 16) || !aligned(q, 16) || (zero_f32 && !aligned(zero_f32, 16)))
+    return MOE_ERR_ALIGN;
+  return status_of(moe::launch_act_quant(M, H, static_cast<const uint16_t*>(x), q, s, zero_f32, stream));
+}
+
+int moe_a8w4_sort(const moe_a8w4_dims* dims, int32_t block_m, const int32_t* topk_ids,
+                  int32_t* sorted_ids, int32_t* block_expert, int32_t* num_padded,
+                  hipStream_t stream) {
+  int st = check_dims(dims);
+  if (st) return st;
+  if (!valid_bm(block_m)) return MOE_ERR_BLOCK_M;
+  if (!num_padded) return MOE_ERR_NULL;
+  if (dims->tokens > 0 && (!topk_ids || !sorted_ids || !block_expert)) return MOE_ERR_NULL;
+  return status_of(moe::launch_sort(topk_ids, dims->tokens, dims->topk, dims->num_experts,
+                                    dims->expert_offset, block_m, sorted_ids, block_expert,
+                                    num_padded, stream));
+}
+
+int moe_a8w4_stage1(const moe_a8w4_dims* dims, int32_t block_m, const uint8_t* a_q,
+                    const uint8_t* a_s, const int32_t* sorted_ids, const int32_t* block_expert,
+                    const int32_t* num_padded, const uint8_t* w13_p, const uint8_t* w13_s_p,
+                    uint8_t* inter_q, uint8_t* inter_s, hipStream_t stream) {
+  int st = check_dims(dims);
+  if (st) return st;
+  if (!valid_bm(block_m)) return MOE_ERR_BLOCK_M;
+  if (dims->tokens == 0) return MOE_OK;
+  const void* ptrs[9] = {a_q, a_s, sorted_ids, block_expert, num_padded, w13_p, w13_s_p, inter_q, inter_s};
+  for (const void* p : ptrs)
+    if (!p) return MOE_ERR_NULL;
+  if (!aligned(a_q, 16) || !aligned(w13_p, 16) || !aligned(w13_s_p, 16) || !aligned(inter_q, 16))
+    return MOE_ERR_ALIGN;
+  const int64_t max_blocks = capacity(dims, block_m) / block_m;
+  return status_of(moe::launch_stage1(stage1_args(dims, block_m, a_q, a_s, sorted_ids, block_expert,
+                                                  num_padded, w13_p, w13_s_p, inter_q, inter_s),
+                                      max_blocks, stream));
+}
+
+int moe_a8w4_stage2(const moe_a8w4_dims* dims, int32_t block_m, const uint8_t* inter_q,
+                    const uint8_t* inter_s, const int32_t* sorted_ids, const int32_t* block_expert,
+                    const int32_t* num_padded, const float* topk_weights, const uint8_t* w2_p,
+                    const uint8_t* w2_s_p, float* acc, hipStream_t stream) {
+  int st = check_dims(dims);
+  if (st) return st;
+  if (!valid_bm(block_m)) return MOE_ERR_BLOCK_M;
+  if (dims->tokens == 0) return MOE_OK;
+  const void* ptrs[10] = {inter_q, inter_s, sorted_ids, block_expert, num_padded, topk_weights,
+                          w2_p, w2_s_p, acc, inter_q};
+  for (const void* p : ptrs)
+    if (!p) return MOE_ERR_NULL;
+  if (!aligned(inter_q, 16) || !aligned(w2_p, 16) || !aligned(w2_s_p, 16) || !aligned(acc, 16))
+    return MOE_ERR_ALIGN;
+  const int64_t max_blocks = capacity(dims, block_m) / block_m;
+  return status_of(moe::launch_stage2(stage2_args(dims, block_m, inter_q, inter_s, sorted_ids,
+                                                  block_expert, num_padded, topk_weights, w2_p,
+                                                  w2_s_p, acc),
+                                      max_blocks, stream));
+}
+
+int moe_a8w4_finalize(int32_t M, int32_t H, const float* acc, void* out, hipStream_t stream) {
+  if (M < 0 || H <= 0 || H % 8 != 0) return MOE_ERR_DIMS;
+  if (M == 0) return MOE_OK;
+  if (!acc || !out) return MOE_ERR_NULL;
+  if (!aligned(acc, 16) || !aligned(out, 16)) return MOE_ERR_ALIGN;
+  return status_of(moe::launch_finalize(M, H, acc, static_cast<uint16_t*>(out), stream));
+}
+
+const char* moe_a8w4_status_str(int status) {
+  switch (status) {
+    case MOE_OK: return "ok";
+    case MOE_ERR_NULL: return "a required pointer is NULL";
+    case MOE_ERR_DIMS: return "a dimension is outside the supported limits";
+    case MOE_ERR_ALIGN: return "a pointer is misaligned (16 B; workspace 256 B)";
+    case MOE_ERR_WORKSPACE: return "workspace smaller than moe_a8w4_workspace_bytes()";
+    case MOE_ERR_BLOCK_M: return "block_m must be 16, 32, 64 or 128";
+    default: return status > 0 ? "HIP launch error (value is a hipError_t)" : "unknown status";
+  }
+}
+
+}  // extern "C"

@@ -1,0 +1,130 @@
+// Bandwidth-bound kernels of the A8W4 MoE layer: the per-1x32 FP8 activation
+// quantiser (with the zero fill of the combine buffer folded in), the final
+// fp32 -> BF16 conversion, and the one-time MXFP4 weight packing.
+//
+// Activation quantisation: FP8 activations with one E8M0 scale per 1x32
+// block (aiter PR 5609, "Add DeepSeek V4.1 Flash TP4 gfx950 MoE tuning",
+// Configuration); the quantisation is part of the timed fused-MoE call (aiter
+// PR 5904, "Add tuned a8w4 fused-MoE configs for DeepSeek V4.1-Flash (TP4 + EP,
+// gfx950)", "Fused-MoE kernel, expert-parallel benchmark").
+#include "common.hpp"
+#include "launch.hpp"
+
+namespace moe {
+
+namespace {
+
+// Four lanes own one 32-element block: lane i of the quad loads 8 BF16 values
+// (16 B), so a wave reads 1 KB contiguous per load and writes 512 B of codes.
+__global__ void __launch_bounds__(256) act_quant_kernel(const uint16_t* __restrict__ x,
+                                                        uint8_t* __restrict__ q,
+                                                        uint8_t* __restrict__ s,
+                                                        float* __restrict__ zero_acc,
+                                                        int64_t n8) {
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n8; i += stride) {
+    // n8 is a multiple of 4 and the stride too, so a quad is either all in or all out
+    const uint4 raw = *reinterpret_cast<const uint4*>(x + i * 8);
+    float v[8];
+    v[0] = bf16_to_f32(raw.x & 0xFFFFu); v[1] = bf16_to_f32(raw.x >> 16);
+    v[2] = bf16_to_f32(raw.y & 0xFFFFu); v[3] = bf16_to_f32(raw.y >> 16);
+    v[4] = bf16_to_f32(raw.z & 0xFFFFu); v[5] = bf16_to_f32(raw.z >> 16);
+    v[6] = bf16_to_f32(raw.w & 0xFFFFu); v[7] = bf16_to_f32(raw.w >> 16);
+    float amax = 0.0f;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) amax = fmaxf(amax, fabsf(v[j]));
+    amax = fmaxf(amax, __shfl_xor(amax, 1));
+    amax = fmaxf(amax, __shfl_xor(amax, 2));
+    const int E = block_exponent(amax);
+    const uint2 codes = encode8(v, exp2_neg(E));
+    *reinterpret_cast<uint2*>(q + i * 8) = codes;
+    if ((i & 3) == 0) s[i >> 2] = (uint8_t)(E + 127);
+    if (zero_acc) {
+      float4* z = reinterpret_cast<float4*>(zero_acc + i * 8);
+      z[0] = make_float4(0.f, 0.f, 0.f, 0.f);
+      z[1] = make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+  }
+}
+
+__global__ void __launch_bounds__(256) finalize_kernel(const float* __restrict__ acc,
+                                                       uint16_t* __restrict__ out, int64_t n8) {
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n8; i += stride) {
+    const float4 a = reinterpret_cast<const float4*>(acc + i * 8)[0];
+    const float4 b = reinterpret_cast<const float4*>(acc + i * 8)[1];
+    uint4 r;
+    r.x = f32_to_bf16(a.x) | (f32_to_bf16(a.y) << 16);
+    r.y = f32_to_bf16(a.z) | (f32_to_bf16(a.w) << 16);
+    r.z = f32_to_bf16(b.x) | (f32_to_bf16(b.y) << 16);
+    r.w = f32_to_bf16(b.z) | (f32_to_bf16(b.w) << 16);
+    *reinterpret_cast<uint4*>(out + i * 8) = r;
+  }
+}
+
+// One thread per (expert, 64-row group, K step, lane): copies the 16-byte K
+// block of each of the lane's four tile rows and gathers their four scales.
+__global__ void __launch_bounds__(256) pack_kernel(const uint8_t* __restrict__ src,
+                                                   const uint8_t* __restrict__ src_s,
+                                                   uint8_t* __restrict__ dst,
+                                                   uint8_t* __restrict__ dst_s, int64_t E,
+                                                   int64_t N, int64_t K) {
+  const int64_t NG = N / 64, KS = K / 128;
+  const int64_t total = E * NG * KS * 64;
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < total; i += stride) {
+    const int lane = (int)(i & 63);
+    int64_t r = i >> 6;
+    const int64_t s = r % KS;
+    r /= KS;
+    const int64_t grp = r % NG;
+    const int64_t e = r / NG;
+    const int m = lane & 15, g = lane >> 4;
+    uint32_t sc = 0;
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      const int64_t n = grp * 64 + pack_row(t, m);
+      const uint8_t* row = src + (e * N + n) * (K / 2);
+      const uint4 v = *reinterpret_cast<const uint4*>(row + 64 * s + 16 * g);
+      *reinterpret_cast<uint4*>(dst + (((e * NG + grp) * KS + s) * 4 + t) * 1024 + lane * 16) = v;
+      sc |= (uint32_t)src_s[(e * N + n) * (K / 32) + 4 * s + g] << (8 * t);
+    }
+    *reinterpret_cast<uint32_t*>(dst_s + (((e * NG + grp) * KS + s) * 64 + lane) * 4) = sc;
+  }
+}
+
+int grid_for(int64_t work, int per_block) {
+  int64_t b = (work + per_block - 1) / per_block;
+  if (b > 4096) b = 4096;
+  if (b < 1) b = 1;
+  return (int)b;
+}
+
+}  // namespace
+
+hipError_t launch_act_quant(int64_t M, int64_t H, const uint16_t* x, uint8_t* q, uint8_t* s,
+                            float* zero_acc, hipStream_t stream) {
+  const int64_t n8 = M * H / 8;
+  if (n8 == 0) return hipSuccess;
+  hipLaunchKernelGGL(act_quant_kernel, dim3(grid_for(n8, 256)), dim3(256), 0, stream, x, q, s,
+                     zero_acc, n8);
+  return hipGetLastError();
+}
+
+hipError_t launch_finalize(int64_t M, int64_t H, const float* acc, uint16_t* out, hipStream_t stream) {
+  const int64_t n8 = M * H / 8;
+  if (n8 == 0) return hipSuccess;
+  hipLaunchKernelGGL(finalize_kernel, dim3(grid_for(n8, 256)), dim3(256), 0, stream, acc, out, n8);
+  return hipGetLastError();
+}
+
+hipError_t launch_pack(const uint8_t* src, const uint8_t* src_s, uint8_t* dst, uint8_t* dst_s,
+                       int64_t E, int64_t N, int64_t K, hipStream_t stream) {
+  const int64_t total = E * (N / 64) * (K / 128) * 64;
+  if (total == 0) return hipSuccess;
+  hipLaunchKernelGGL(pack_kernel, dim3(grid_for(total, 256)), dim3(256), 0, stream, src, src_s, dst,
+                     dst_s, E, N, K);
+  return hipGetLastError();
+}
+
+}  // namespace moe

@@ -1,0 +1,41 @@
+// Internal launchers of the A8W4 MoE kernels (host side).  Arguments are
+// validated by the C ABI in api.hip before any of these is called.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace moe {
+
+struct GemmArgs {
+  int32_t M;              // tokens
+  int32_t topk;
+  int32_t N;              // rows of the expert weight matrix (2I for stage 1, H for stage 2)
+  int32_t K;              // reduction length (H for stage 1, I for stage 2)
+  int32_t bm;             // rows per sorted block
+  const int32_t* sorted_ids;
+  const int32_t* block_expert;
+  const int32_t* num_padded;
+  const uint8_t* bq;      // B rows: token activations (stage 1) or sorted intermediate (stage 2), [.., K]
+  const uint8_t* bs;      // their E8M0 scales [.., K/32]
+  const uint8_t* w;       // packed expert weights, N*K/2 bytes per expert
+  const uint8_t* ws;      // packed scales, N*K/32 bytes per expert
+  uint8_t* out_q;         // stage 1: intermediate codes [P, N/2]
+  uint8_t* out_s;         // stage 1: intermediate scales [P, N/64]
+  const float* topk_weights;  // stage 2: [M, topk]
+  float* acc;             // stage 2: fp32 combine buffer [M, K_out = N]
+};
+
+hipError_t launch_act_quant(int64_t M, int64_t H, const uint16_t* x, uint8_t* q, uint8_t* s,
+                            float* zero_acc, hipStream_t stream);
+hipError_t launch_sort(const int32_t* ids, int32_t M, int32_t topk, int32_t E, int32_t expert_offset,
+                       int32_t bm, int32_t* sorted_ids, int32_t* block_expert, int32_t* num_padded,
+                       hipStream_t stream);
+hipError_t launch_finalize(int64_t M, int64_t H, const float* acc, uint16_t* out, hipStream_t stream);
+hipError_t launch_pack(const uint8_t* src, const uint8_t* src_s, uint8_t* dst, uint8_t* dst_s,
+                       int64_t E, int64_t N, int64_t K, hipStream_t stream);
+// max_blocks: upper bound of sorted blocks (grid size); kernels read the real count on device
+hipError_t launch_stage1(const GemmArgs& a, int64_t max_blocks, hipStream_t stream);
+hipError_t launch_stage2(const GemmArgs& a, int64_t max_blocks, hipStream_t stream);
+
+}  // namespace moe

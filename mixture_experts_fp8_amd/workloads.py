@@ -95,10 +95,17 @@ def make_weights(w: Workload, seed=None):
     """(w13 [E,2I,H/2], w13_s [E,2I,H/32], w2 [E,H,I/2], w2_s [E,H,I/32]) as uint8."""
     rng = np.random.default_rng([w.config_id, 1] if seed is None else seed)
     E, H, I, Iv = w.num_experts, w.hidden, w.inter, w.inter_valid
-    w13 = rng.integers(0, 256, size=(E, 2 * I, H // 2), dtype=np.uint8)
-    w13_s = rng.choice(np.array(WEIGHT_SCALE_CODES, np.uint8), size=(E, 2 * I, H // 32))
-    w2 = rng.integers(0, 256, size=(E, H, I // 2), dtype=np.uint8)
-    w2_s = rng.choice(np.array(WEIGHT_SCALE_CODES, np.uint8), size=(E, H, I // 32))
+    lo, hi = WEIGHT_SCALE_CODES[0], WEIGHT_SCALE_CODES[-1] + 1
+
+    def codes(shape):  # uniform random bytes = two independent uniform E2M1 codes
+        n = int(np.prod(shape))
+        raw = rng.bit_generator.random_raw((n + 7) // 8).view(np.uint8)
+        return raw[:n].reshape(shape)
+
+    w13 = codes((E, 2 * I, H // 2))
+    w13_s = rng.integers(lo, hi, size=(E, 2 * I, H // 32), dtype=np.uint8)
+    w2 = codes((E, H, I // 2))
+    w2_s = rng.integers(lo, hi, size=(E, H, I // 32), dtype=np.uint8)
     if Iv < I:
         w13[:, 2 * Iv:, :] = 0          # gate/up rows of the padded columns
         w2[:, :, Iv // 2:] = 0          # down-projection columns past the valid width

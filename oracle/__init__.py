@@ -78,6 +78,9 @@ def _load():
     lib.oracle_intermediate.argtypes = ([c_i64, c_i64, c_i64, c_int, c_int, c_int] + [vp] * 4
                                         + [vp, c_i64, vp, vp, vp])
     lib.oracle_intermediate.restype = None
+    lib.oracle_forward_given_intermediate.argtypes = ([c_i64, c_i64, c_i64, c_int, c_int, c_int]
+                                                      + [vp] * 4 + [vp, c_i64, vp, vp, vp, vp])
+    lib.oracle_forward_given_intermediate.restype = None
     lib.oracle_num_threads.argtypes = []
     lib.oracle_num_threads.restype = c_int
     _lib = lib
@@ -227,6 +230,37 @@ def intermediate(hidden_bf16, topk_ids, w13, w13_s, routes, expert_offset: int =
     _load().oracle_intermediate(M, H, I, E, expert_offset, k, _p(x), _p(ids), _p(w13), _p(w13_s),
                                 _p(r), n, _p(h), _p(iq), _p(is_))
     return (iq, is_, h) if want_f64 else (iq, is_)
+
+
+def forward_given_intermediate(topk_ids, topk_weights, w2, w2_s, inter_q, inter_s,
+                               expert_offset: int = 0, tokens=None, want_f64: bool = False):
+    """Stage two and the combine applied to a given intermediate.
+
+    inter_q [ntok, topk, I] / inter_s [ntok, topk, I/32] hold the requantised
+    intermediate of each listed token's slots (non-local slots are ignored).
+    Returns out_bf16 [ntok, H] (and the FP64 combine if want_f64).
+    """
+    ids = _c(topk_ids, np.int32)
+    wts = _c(topk_weights, np.float32)
+    w2 = _c(w2, np.uint8)
+    w2_s = _c(w2_s, np.uint8)
+    iq = _c(inter_q, np.uint8)
+    is_ = _c(inter_s, np.uint8)
+    M, k = ids.shape
+    E, H = w2.shape[0], w2.shape[1]
+    I = w2.shape[2] * 2
+    if tokens is None:
+        tok, ntok = None, M
+    else:
+        tok = _c(tokens, np.int64)
+        ntok = tok.shape[0]
+    assert iq.shape == (ntok, k, I) and is_.shape == (ntok, k, I // 32)
+    out = np.zeros((ntok, H), np.uint16)
+    o64 = np.zeros((ntok, H), np.float64) if want_f64 else None
+    _load().oracle_forward_given_intermediate(M, H, I, E, expert_offset, k, _p(ids), _p(wts),
+                                              _p(w2), _p(w2_s), _p(tok), ntok, _p(iq), _p(is_),
+                                              _p(o64), _p(out))
+    return (out, o64) if want_f64 else out
 
 
 def num_threads() -> int:

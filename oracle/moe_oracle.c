@@ -244,27 +244,25 @@ static inline double mxfp4_elem(const uint8_t* codes, const uint8_t* scales,
     return g_e2m1_all[c] * g_e8m0_all[scales[row * (K / 32) + kk / 32]];
 }
 
-/* Stage one, activation and intermediate requantisation, and stage two for
- * one route of token t to local expert e.
+/* Stage one and the intermediate requantisation for one route of a token to
+ * local expert e.
  *   a_q/a_s : the token's quantised activation row (H codes, H/32 scales)
+ *   w13/_s  : expert e's gate/up matrix [2I, H/2] and scales [2I, H/32]
  *   h       : out, I values of SiLU(gate) * up in FP64 (may be NULL)
  *   iq, is  : out, the requantised intermediate (I codes, I/32 scales)
- *   y       : out, H values of the stage-two product in FP64 (may be NULL)
  */
-void oracle_route(int64_t H, int64_t I,
-                  const uint8_t* a_q, const uint8_t* a_s,
-                  const uint8_t* w13, const uint8_t* w13_s,
-                  const uint8_t* w2, const uint8_t* w2_s,
-                  double* h, uint8_t* iq, uint8_t* is, double* y)
+void oracle_stage1(int64_t H, int64_t I,
+                   const uint8_t* a_q, const uint8_t* a_s,
+                   const uint8_t* w13, const uint8_t* w13_s,
+                   double* h, uint8_t* iq, uint8_t* is)
 {
     e4m3_table_init();
     double* a = (double*)malloc(sizeof(double) * H);
     double* hv = (double*)malloc(sizeof(double) * I);
-    double* iv = (double*)malloc(sizeof(double) * I);
     for (int64_t kk = 0; kk < H; ++kk)
         a[kk] = g_e4m3_all[a_q[kk]] * g_e8m0_all[a_s[kk / 32]];
 
-    /* stage one: g_j from row 2j, u_j from row 2j+1; SiLU(g) * u */
+    /* g_j from row 2j, u_j from row 2j+1; SiLU(g) * u */
     for (int64_t j = 0; j < I; ++j) {
         double g = 0.0, u = 0.0;
         for (int64_t kk = 0; kk < H; ++kk) {
@@ -277,20 +275,60 @@ void oracle_route(int64_t H, int64_t I,
 
     /* intermediate quantisation, per 1x32 along j */
     for (int64_t c = 0; c < I / 32; ++c) oracle_quant_block(hv + 32 * c, 32, iq + 32 * c, is + c);
-    for (int64_t j = 0; j < I; ++j)
-        iv[j] = g_e4m3_all[iq[j]] * g_e8m0_all[is[j / 32]];
-
-    /* stage two: y_h = sum_j inter_j * w2[h, j] */
-    if (y) {
-        for (int64_t hh = 0; hh < H; ++hh) {
-            double acc = 0.0;
-            for (int64_t j = 0; j < I; ++j) acc += iv[j] * mxfp4_elem(w2, w2_s, I, hh, j);
-            y[hh] = acc;
-        }
-    }
     free(a);
     free(hv);
+}
+
+/* Stage two for one route: y_h = sum_j inter_j * w2[e][h, j] in FP64, with
+ * inter the dequantised intermediate (I codes, I/32 scales). */
+void oracle_stage2(int64_t H, int64_t I, const uint8_t* iq, const uint8_t* is,
+                   const uint8_t* w2, const uint8_t* w2_s, double* y)
+{
+    e4m3_table_init();
+    double* iv = (double*)malloc(sizeof(double) * I);
+    for (int64_t j = 0; j < I; ++j)
+        iv[j] = g_e4m3_all[iq[j]] * g_e8m0_all[is[j / 32]];
+    for (int64_t hh = 0; hh < H; ++hh) {
+        double acc = 0.0;
+        for (int64_t j = 0; j < I; ++j) acc += iv[j] * mxfp4_elem(w2, w2_s, I, hh, j);
+        y[hh] = acc;
+    }
     free(iv);
+}
+
+/* Both stages for one route (y may be NULL to stop after the requantisation). */
+void oracle_route(int64_t H, int64_t I,
+                  const uint8_t* a_q, const uint8_t* a_s,
+                  const uint8_t* w13, const uint8_t* w13_s,
+                  const uint8_t* w2, const uint8_t* w2_s,
+                  double* h, uint8_t* iq, uint8_t* is, double* y)
+{
+    oracle_stage1(H, I, a_q, a_s, w13, w13_s, h, iq, is);
+    if (y) oracle_stage2(H, I, iq, is, w2, w2_s, y);
+}
+
+/* Combine: o[t] = sum over local slots k, ascending, of w[t,k] * y[t,k] in
+ * FP64 (the routing weight is applied here, after stage two), then BF16.
+ * y holds [ntok, topk, H]; non-local slots are skipped. */
+static void combine(int64_t H, int E, int expert_offset, int topk,
+                    const int32_t* topk_ids, const float* topk_weights,
+                    const int64_t* tokens, int64_t ntok, const double* y,
+                    double* out_f64, uint16_t* out_bf16)
+{
+#pragma omp parallel for schedule(static)
+    for (int64_t i = 0; i < ntok; ++i) {
+        int64_t t = tokens ? tokens[i] : i;
+        for (int64_t hh = 0; hh < H; ++hh) {
+            double o = 0.0;
+            for (int k = 0; k < topk; ++k) {
+                int64_t le = (int64_t)topk_ids[t * topk + k] - expert_offset;
+                if (le < 0 || le >= E) continue;
+                o += (double)topk_weights[t * topk + k] * y[(i * topk + k) * H + hh];
+            }
+            if (out_f64) out_f64[i * H + hh] = o;
+            out_bf16[i * H + hh] = oracle_bf16_rne(o);
+        }
+    }
 }
 
 /* ------------------------------------------------------------ whole layer */
@@ -335,21 +373,36 @@ void oracle_forward(int64_t M, int64_t H, int64_t I, int E, int expert_offset, i
                      NULL, iq, is, y + r * H);
         free(aq); free(as); free(iq); free(is);
     }
-    /* combine: sum over local slots in ascending k, weight applied here */
-#pragma omp parallel for schedule(static)
-    for (int64_t i = 0; i < ntok; ++i) {
+    combine(H, E, expert_offset, topk, topk_ids, topk_weights, tokens, ntok, y, out_f64, out_bf16);
+    free(y);
+}
+
+/* Stage two and the combine of oracle_forward, applied to a given
+ * requantised intermediate instead of the one stage one would produce:
+ *   inter_q [ntok, topk, I], inter_s [ntok, topk, I/32] for the listed tokens'
+ *   slots (rows of non-local slots are ignored).
+ * Used to check the output given another implementation's intermediate. */
+void oracle_forward_given_intermediate(int64_t M, int64_t H, int64_t I, int E, int expert_offset,
+                                       int topk, const int32_t* topk_ids, const float* topk_weights,
+                                       const uint8_t* w2, const uint8_t* w2_s,
+                                       const int64_t* tokens, int64_t ntok,
+                                       const uint8_t* inter_q, const uint8_t* inter_s,
+                                       double* out_f64, uint16_t* out_bf16)
+{
+    e4m3_table_init();
+    if (!tokens) ntok = M;
+    int64_t nroute = ntok * topk;
+    double* y = (double*)calloc((size_t)(nroute > 0 ? nroute : 1) * H, sizeof(double));
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t r = 0; r < nroute; ++r) {
+        int64_t i = r / topk, k = r % topk;
         int64_t t = tokens ? tokens[i] : i;
-        for (int64_t hh = 0; hh < H; ++hh) {
-            double o = 0.0;
-            for (int k = 0; k < topk; ++k) {
-                int64_t le = (int64_t)topk_ids[t * topk + k] - expert_offset;
-                if (le < 0 || le >= E) continue;
-                o += (double)topk_weights[t * topk + k] * y[(i * topk + k) * H + hh];
-            }
-            if (out_f64) out_f64[i * H + hh] = o;
-            out_bf16[i * H + hh] = oracle_bf16_rne(o);
-        }
+        int64_t le = (int64_t)topk_ids[t * topk + k] - expert_offset;
+        if (le < 0 || le >= E) continue;
+        oracle_stage2(H, I, inter_q + r * I, inter_s + r * (I / 32),
+                      w2 + le * H * (I / 2), w2_s + le * H * (I / 32), y + r * H);
     }
+    combine(H, E, expert_offset, topk, topk_ids, topk_weights, tokens, ntok, y, out_f64, out_bf16);
     free(y);
 }
 

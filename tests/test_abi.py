@@ -1,0 +1,107 @@
+"""The C ABI library loads, exports every symbol its header declares, and
+rejects invalid arguments on the host before any GPU work (no GPU needed)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from mixture_experts_fp8_amd import abi
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "moe_a8w4.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(moe_a8w4_[a-z_0-9]+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_symbol():
+    lib = abi.load()
+    names = declared_functions()
+    assert len(names) >= 11
+    assert set(names) == set(abi.EXPORTS)
+    for n in names:
+        assert getattr(lib, n) is not None
+
+
+def dims(**kw):
+    d = dict(tokens=5, hidden=5120, inter=640, num_experts=128, topk=3, expert_offset=0)
+    d.update(kw)
+    return abi.make_dims(d["tokens"], d["hidden"], d["inter"], d["num_experts"], d["topk"],
+                         d["expert_offset"])
+
+
+@pytest.mark.parametrize("bad", [
+    dict(tokens=-1), dict(tokens=1 << 24), dict(hidden=0), dict(hidden=5000), dict(hidden=256),
+    dict(inter=0), dict(inter=576), dict(inter=64), dict(num_experts=0), dict(num_experts=513),
+    dict(topk=0), dict(topk=9),
+])
+def test_invalid_dims_rejected(bad):
+    lib = abi.load()
+    d = dims(**bad)
+    n = ctypes.c_size_t(0)
+    assert lib.moe_a8w4_workspace_bytes(ctypes.byref(d), ctypes.byref(n)) == abi.MOE_ERR_DIMS
+    assert lib.moe_a8w4_block_m(ctypes.byref(d)) == abi.MOE_ERR_DIMS
+    one = ctypes.c_void_p(256)
+    st = lib.moe_a8w4_forward(ctypes.byref(d), *([one] * 9), 1 << 40, None)
+    assert st == abi.MOE_ERR_DIMS
+
+
+def test_null_dims_and_pointers():
+    lib = abi.load()
+    assert lib.moe_a8w4_block_m(None) == abi.MOE_ERR_NULL
+    d = dims()
+    one = ctypes.c_void_p(256)
+    for i in range(9):
+        ptrs = [one] * 9
+        ptrs[i] = None
+        assert lib.moe_a8w4_forward(ctypes.byref(d), *ptrs, 1 << 40, None) == abi.MOE_ERR_NULL
+
+
+def test_misaligned_and_small_workspace():
+    lib = abi.load()
+    d = dims()
+    ok = ctypes.c_void_p(4096)
+    bad = ctypes.c_void_p(4096 + 8)
+    need = abi.moe_a8w4_workspace_bytes(d)
+    assert lib.moe_a8w4_forward(ctypes.byref(d), bad, *([ok] * 8), need, None) == abi.MOE_ERR_ALIGN
+    ws_bad = ctypes.c_void_p(4096 + 16)   # 16-byte but not 256-byte aligned
+    assert lib.moe_a8w4_forward(ctypes.byref(d), *([ok] * 8), ws_bad, need, None) == abi.MOE_ERR_ALIGN
+    assert lib.moe_a8w4_forward(ctypes.byref(d), *([ok] * 9), need - 1, None) == abi.MOE_ERR_WORKSPACE
+
+
+def test_zero_tokens_is_a_noop():
+    lib = abi.load()
+    d = dims(tokens=0)
+    assert lib.moe_a8w4_forward(ctypes.byref(d), *([None] * 9), 0, None) == abi.MOE_OK
+
+
+def test_block_m_capacity_and_workspace_sizes():
+    assert abi.moe_a8w4_block_m(dims(tokens=5)) == 16
+    assert abi.moe_a8w4_block_m(dims(tokens=768, num_experts=384, topk=6)) == 32
+    assert abi.moe_a8w4_block_m(dims(tokens=16384, num_experts=96, topk=6, inter=2304)) == 128
+    d = dims(tokens=33, num_experts=384, topk=6)
+    R = 33 * 6
+    for bm in (16, 32, 64, 128):
+        cap = abi.moe_a8w4_sort_capacity(d, bm)
+        assert cap % bm == 0 and cap >= R + min(384, R) * (bm - 1)
+    with pytest.raises(abi.MoeError):
+        abi.moe_a8w4_sort_capacity(d, 48)
+    ws = abi.moe_a8w4_workspace_bytes(dims(tokens=16384, num_experts=385, topk=7))
+    assert ws < 1 << 30
+    assert "block_m" in abi.status_str(abi.MOE_ERR_BLOCK_M)
+
+
+def test_step_entry_points_validate():
+    lib = abi.load()
+    d = dims()
+    p = ctypes.c_void_p(4096)
+    assert lib.moe_a8w4_sort(ctypes.byref(d), 48, p, p, p, p, None) == abi.MOE_ERR_BLOCK_M
+    assert lib.moe_a8w4_stage1(ctypes.byref(d), 16, *([p] * 8), None, None) == abi.MOE_ERR_NULL
+    assert lib.moe_a8w4_stage2(ctypes.byref(d), 16, *([p] * 8), None, None) == abi.MOE_ERR_NULL
+    assert lib.moe_a8w4_quant_act(4, 48, p, p, p, None, None) == abi.MOE_ERR_DIMS
+    assert lib.moe_a8w4_finalize(4, 5120, p, None, None) == abi.MOE_ERR_NULL
+    assert lib.moe_a8w4_pack_weights(ctypes.byref(d), *([p] * 7), None, None) == abi.MOE_ERR_NULL

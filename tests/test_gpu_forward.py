@@ -1,0 +1,185 @@
+"""GPU parity of the whole layer through the C ABI against the oracle, at the
+gate of the pages' validation (atol = rtol = 2e-2, all outputs finite):
+small geometries on every token, the five workloads at full size on sampled
+tokens, edge cases, input preservation, the step entry points, and replays
+of a captured graph on changed inputs."""
+import numpy as np
+import pytest
+import torch
+
+from mixture_experts_fp8_amd import abi, workloads as wl
+from gpu_util import DEV, Layer, assert_gate, check_forward, dev, host_bf16_bits, note
+
+pytestmark = pytest.mark.gpu
+
+
+SMALL = [
+    ("draft-decode", 8, 5, "softmax"),
+    ("draft-decode", 8, 1, "softmax"),
+    ("draft-sweep", 12, 40, "concentrated"),
+    ("backbone-decode", 24, 31, "softmax"),
+    ("backbone-decode", 24, 33, "softmax"),
+    ("backbone-decode", 24, 257, "softmax"),
+    ("local-slice", 8, 16, "softmax"),
+    ("prefill-shared", 9, 70, "roundrobin"),
+]
+
+
+@pytest.mark.parametrize("name,E,M,mode", SMALL)
+def test_forward_small_all_tokens(name, E, M, mode):
+    base = wl.WORKLOADS[name]
+    routed = E - 1 if base.shared else E
+    w = wl.scaled(base, num_experts=E, routed_experts=routed, config_id=100 + E)
+    if name == "local-slice":
+        w = wl.scaled(w, routed_experts=4 * E)   # a quarter of the routes are local
+    layer = Layer(w)
+    hidden, ids, wts = wl.make_inputs(w, M, mode)
+    note("forward %s E=%d M=%d %s bm=%d" % (name, E, M, mode, abi.moe_a8w4_block_m(layer.dims(M))))
+    out = torch.full((M, w.hidden), float("nan"), dtype=torch.bfloat16, device=DEV)
+    xd, idd = dev(hidden), dev(ids)
+    layer.forward(xd, idd, wts, out=out)
+    torch.cuda.synchronize()
+    check_forward(layer, hidden, ids, wts, host_bf16_bits(out), xd, idd)
+
+
+FULL = [("draft-decode", 5, "softmax"), ("backbone-decode", 768, "softmax"),
+        ("backbone-decode", 256, "softmax"), ("draft-sweep", 640, "concentrated"),
+        ("local-slice", 1024, "softmax"), ("local-slice", 16384, "softmax"),
+        ("prefill-shared", 4096, "roundrobin"), ("prefill-shared", 16384, "softmax")]
+
+
+@pytest.fixture(scope="module")
+def layers():
+    cache = {}
+
+    def get(name):
+        if name not in cache:
+            cache.clear()
+            torch.cuda.empty_cache()
+            cache[name] = Layer(wl.WORKLOADS[name])
+        return cache[name]
+
+    yield get
+    cache.clear()
+
+
+@pytest.mark.parametrize("name,M,mode", FULL)
+def test_forward_full_size_sampled(layers, name, M, mode):
+    layer = layers(name)
+    w = layer.w
+    hidden, ids, wts = wl.make_inputs(w, M, mode)
+    note("forward full %s M=%d %s bm=%d" % (name, M, mode, abi.moe_a8w4_block_m(layer.dims(M))))
+    out = torch.full((M, w.hidden), float("nan"), dtype=torch.bfloat16, device=DEV)
+    xd, idd, wd = dev(hidden), dev(ids), dev(wts)
+    layer.forward(xd, idd, wd, out=out)
+    torch.cuda.synchronize()
+    bits = host_bf16_bits(out)
+    vals = wl.bf16_to_f32(bits)
+    assert np.isfinite(vals).all()
+    # tokens with no local route are exact zeros
+    le = ids.astype(np.int64) - w.expert_offset
+    none_local = ~((le >= 0) & (le < w.num_experts)).any(axis=1)
+    assert np.all(vals[none_local] == 0)
+    # sampled rows against the oracle: first, last and random ones
+    rng = np.random.default_rng(M)
+    n = 4 if M >= 4096 else 6
+    tok = np.unique(np.concatenate([[0, M - 1], rng.integers(0, M, n)])).astype(np.int64)
+    check_forward(layer, hidden, ids, wts, bits, xd, idd, tokens=tok)
+    # inputs unchanged
+    assert np.array_equal(host_bf16_bits(xd), hidden)
+    assert np.array_equal(idd.cpu().numpy(), ids)
+    assert np.array_equal(wd.cpu().numpy(), wts)
+
+
+def test_edge_cases():
+    w = wl.scaled(wl.WORKLOADS["backbone-decode"], num_experts=12, routed_experts=12, config_id=120)
+    layer = Layer(w)
+    M = 9
+    hidden, ids, wts = wl.make_inputs(w, M, "softmax")
+    # a token whose routes are all non-local, negative and too-large ids, a duplicate
+    ids = ids.copy()
+    ids[0, :] = -1
+    ids[1, 2] = 500
+    ids[2, 1] = ids[2, 0]
+    note("edge cases M=%d" % M)
+    xd, idd = dev(hidden), dev(ids)
+    out = layer.forward(xd, idd, wts)
+    torch.cuda.synchronize()
+    bits = host_bf16_bits(out)
+    assert np.all(bits[0] == 0)
+    check_forward(layer, hidden, ids, wts, bits, xd, idd)
+    # expert_offset: the same experts addressed as a slice at 192
+    w2 = wl.scaled(w, expert_offset=192)
+    layer2 = Layer(w2, weights=layer.host)
+    out2 = layer2.forward(hidden, np.where(ids >= 0, ids + 192, ids).astype(np.int32), wts)
+    torch.cuda.synchronize()
+    assert_gate(wl.bf16_to_f32(host_bf16_bits(out2)), wl.bf16_to_f32(bits), "offset")
+    # M = 0 is a no-op
+    d0 = layer.dims(0)
+    assert abi.load().moe_a8w4_forward(d0, *([None] * 9), 0, None) == abi.MOE_OK
+
+
+def test_steps_compose_to_forward():
+    w = wl.scaled(wl.WORKLOADS["draft-sweep"], num_experts=16, routed_experts=16, config_id=121)
+    layer = Layer(w)
+    M = 80
+    hidden, ids, wts = wl.make_inputs(w, M, "softmax")
+    d = layer.dims(M)
+    bm = abi.moe_a8w4_block_m(d)
+    note("steps M=%d bm=%d" % (M, bm))
+    xd, idd, wd = dev(hidden), dev(ids), dev(wts)
+    acc = torch.empty((M, w.hidden), dtype=torch.float32, device=DEV)
+    q, s = abi.moe_a8w4_quant_act(xd, zero_f32=acc)
+    srt, bexp, npad = abi.moe_a8w4_sort(d, bm, idd)
+    iq, is_ = abi.moe_a8w4_stage1(d, bm, q, s, srt, bexp, npad, layer.packed[0], layer.packed[1])
+    abi.moe_a8w4_stage2(d, bm, iq, is_, srt, bexp, npad, wd, layer.packed[2], layer.packed[3], acc)
+    out_steps = abi.moe_a8w4_finalize(acc)
+    out_fwd = layer.forward(xd, idd, wd)
+    torch.cuda.synchronize()
+    a = out_steps.float().cpu().numpy()
+    b = out_fwd.float().cpu().numpy()
+    # same kernels; only the order of the fp32 top-k additions may differ
+    assert np.allclose(a, b, rtol=2 ** -7, atol=1e-6)
+    check_forward(layer, hidden, ids, wts, host_bf16_bits(out_fwd), xd, idd)
+
+
+def test_graph_replay_on_changed_inputs():
+    """Capture one call; replay it on original, changed, concentrated and
+    restored inputs written into the captured buffers; each replay matches
+    the eager call on the same inputs and the oracle."""
+    w = wl.scaled(wl.WORKLOADS["draft-sweep"], num_experts=16, routed_experts=16, config_id=122)
+    layer = Layer(w)
+    M = 40
+    cases = {
+        "original": wl.make_inputs(w, M, "softmax", seed=[1]),
+        "changed": wl.make_inputs(w, M, "softmax", seed=[2]),
+        "concentrated": wl.make_inputs(w, M, "concentrated", seed=[3]),
+    }
+    cases["restored"] = cases["original"]
+    d = layer.dims(M)
+    ws = torch.empty(abi.moe_a8w4_workspace_bytes(d), dtype=torch.uint8, device=DEV)
+    xd, idd, wd = dev(cases["original"][0]), dev(cases["original"][1]), dev(cases["original"][2])
+    out = torch.empty((M, w.hidden), dtype=torch.bfloat16, device=DEV)
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        layer.forward(xd, idd, wd, out=out, workspace=ws)      # warm-up outside capture
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        layer.forward(xd, idd, wd, out=out, workspace=ws)
+    torch.cuda.synchronize()
+    for name, (h, i, wt) in cases.items():
+        note("graph replay %s" % name)
+        xd.copy_(dev(h))
+        idd.copy_(dev(i))
+        wd.copy_(dev(wt))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        got = out.float().cpu().numpy()
+        eager = layer.forward(dev(h), dev(i), dev(wt)).float().cpu().numpy()
+        torch.cuda.synchronize()
+        assert np.allclose(got, eager, rtol=2 ** -7, atol=1e-6), name
+        check_forward(layer, h, i, wt, host_bf16_bits(out), xd, idd)

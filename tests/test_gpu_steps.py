@@ -1,0 +1,157 @@
+"""GPU parity of the single steps through the C ABI: activation quantisation
+and the sort bit-exact against the oracle, the weight packing against its
+stated permutation, and the stage-one intermediate within one FP8 quantum."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from mixture_experts_fp8_amd import abi, workloads as wl
+from gpu_util import DEV, Layer, check_intermediate, dev, note
+
+pytestmark = pytest.mark.gpu
+
+
+def finite_bf16_blocks(cols, seed=0):
+    bits = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    bits = bits[((bits >> 7) & 0xFF) != 0xFF]
+    rng = np.random.default_rng(seed)
+    bits = rng.permutation(bits)
+    n = (len(bits) + cols - 1) // cols * cols
+    out = np.zeros(n, np.uint16)
+    out[: len(bits)] = bits
+    return out.reshape(-1, cols)
+
+
+@pytest.mark.parametrize("case", ["exhaustive-bf16", "normal-257x5120", "ones-3x512"])
+def test_quant_act_bit_exact(case):
+    if case == "exhaustive-bf16":
+        x = finite_bf16_blocks(1024)
+    elif case == "normal-257x5120":
+        x = wl.make_hidden(np.random.default_rng(3), 257, 5120)
+    else:
+        x = wl.bf16_bits(np.ones((3, 512), np.float32))
+    note("quant_act %s %s" % (case, x.shape))
+    xd = dev(x)
+    zero = torch.full(x.shape, 7.0, dtype=torch.float32, device=DEV)
+    q, s = abi.moe_a8w4_quant_act(xd, zero_f32=zero)
+    torch.cuda.synchronize()
+    rq, rs = oracle.quant_act(x)
+    assert np.array_equal(q.cpu().numpy(), rq)
+    assert np.array_equal(s.cpu().numpy(), rs)
+    assert torch.count_nonzero(zero).item() == 0
+
+
+SORT_CASES = []
+for name, Ms in [("backbone-decode", (1, 6, 31, 32, 33, 255, 256, 257, 768)),
+                 ("draft-sweep", (5, 640)), ("local-slice", (16, 4096, 16384)),
+                 ("prefill-shared", (4096, 16384))]:
+    for M in Ms:
+        for bm in (16, 32, 64, 128):
+            SORT_CASES.append((name, M, bm))
+
+
+@pytest.mark.parametrize("name,M,bm", SORT_CASES)
+def test_sort_bit_exact(name, M, bm):
+    w = wl.WORKLOADS[name]
+    mode = w.routings[-1]
+    _, ids, _ = wl.make_inputs(wl.scaled(w, hidden=32), M, mode)
+    note("sort %s M=%d bm=%d mode=%s" % (name, M, bm, mode))
+    d = abi.make_dims(M, 5120, 640, w.num_experts, w.topk, w.expert_offset)
+    s, b, n = abi.moe_a8w4_sort(d, bm, dev(ids))
+    torch.cuda.synchronize()
+    rs, rb = oracle.sort(ids, w.num_experts, w.expert_offset, bm)
+    P = int(n.item())
+    assert P == len(rs)
+    assert np.array_equal(s[:P].cpu().numpy(), rs)
+    assert np.array_equal(b[: P // bm].cpu().numpy(), rb)
+
+
+def test_sort_nonlocal_duplicates_offset_and_repeatability():
+    rng = np.random.default_rng(8)
+    M, k, E, off, bm = 300, 6, 96, 192, 32
+    ids = rng.integers(-10, 500, size=(M, k)).astype(np.int32)
+    ids[5, 1] = ids[5, 0]
+    ids[7, :] = 1000                       # a token with no local route
+    d = abi.make_dims(M, 5120, 640, E, k, off)
+    rs, rb = oracle.sort(ids, E, off, bm)
+    idd = dev(ids)
+    first = None
+    for rep in range(20):
+        s, b, n = abi.moe_a8w4_sort(d, bm, idd)
+        torch.cuda.synchronize()
+        P = int(n.item())
+        got = (s[:P].cpu().numpy(), b[: P // bm].cpu().numpy())
+        assert np.array_equal(got[0], rs) and np.array_equal(got[1], rb)
+        if first is None:
+            first = got
+    # no local route at all
+    s, b, n = abi.moe_a8w4_sort(d, bm, dev(np.full((M, k), 5, np.int32)))
+    torch.cuda.synchronize()
+    assert int(n.item()) == 0
+
+
+def test_pack_layout():
+    """Packed codes/scales equal the documented permutation of the inputs."""
+    E, H, I = 2, 512, 256
+    w = wl.Workload("pack", H, I, I, E, E, 2, False, 0, (), ("softmax",), 55)
+    w13, w13_s, w2, w2_s = wl.make_weights(w)
+    d = abi.make_dims(1, H, I, E, 2)
+    p13, p13s, p2, p2s = [t.cpu().numpy() for t in abi.moe_a8w4_pack_weights(
+        d, dev(w13), dev(w13_s), dev(w2), dev(w2_s))]
+
+    def expect(codes, scales, N, K):
+        KS, NG = K // 128, N // 64
+        ec = np.zeros(codes.size, np.uint8)
+        es = np.zeros(scales.size, np.uint8)
+        for e in range(E):
+            for g in range(NG):
+                for s in range(KS):
+                    for t in range(4):
+                        for lane in range(64):
+                            m, q = lane % 16, lane // 16
+                            n = g * 64 + 16 * (m // 4) + 4 * t + (m % 4)
+                            dst = ((((e * NG + g) * KS + s) * 4 + t) * 64 + lane) * 16
+                            ec[dst:dst + 16] = codes[e, n, 64 * s + 16 * q: 64 * s + 16 * q + 16]
+                            es[(((e * NG + g) * KS + s) * 64 + lane) * 4 + t] = scales[e, n, 4 * s + q]
+        return ec, es
+
+    ec, es = expect(w13, w13_s, 2 * I, H)
+    assert np.array_equal(p13.ravel(), ec) and np.array_equal(p13s.ravel(), es)
+    ec, es = expect(w2, w2_s, H, I)
+    assert np.array_equal(p2.ravel(), ec) and np.array_equal(p2s.ravel(), es)
+
+
+@pytest.mark.parametrize("name,M,E", [("draft-decode", 33, 8), ("local-slice", 40, 6),
+                                      ("backbone-decode", 257, 16)])
+def test_stage1_intermediate(name, M, E):
+    """Stage one against the oracle's requantised intermediate, route by route.
+
+    The GPU intermediate must be a faithful rounding of the oracle's exact
+    value (see gpu_util.check_intermediate), and rows holding a route must be
+    fully written: the buffers start as 0xFF, which no code or scale takes.
+    """
+    w = wl.scaled(wl.WORKLOADS[name], num_experts=E, routed_experts=E, config_id=60 + E)
+    L = Layer(w)
+    hidden, ids, wts = wl.make_inputs(w, M, "softmax")
+    note("stage1 %s M=%d E=%d" % (name, M, E))
+    d = L.dims(M)
+    bm = abi.moe_a8w4_block_m(d)
+    q, s = abi.moe_a8w4_quant_act(dev(hidden))
+    srt, bexp, npad = abi.moe_a8w4_sort(d, bm, dev(ids))
+    cap = abi.moe_a8w4_sort_capacity(d, bm)
+    iq = torch.full((cap, w.inter), 0xFF, dtype=torch.uint8, device=DEV)
+    is_ = torch.full((cap, w.inter // 32), 0xFF, dtype=torch.uint8, device=DEV)
+    abi.moe_a8w4_stage1(d, bm, q, s, srt, bexp, npad, L.packed[0], L.packed[1], iq, is_)
+    torch.cuda.synchronize()
+    P = int(npad.item())
+    sorted_ids = srt[:P].cpu().numpy()
+    real = np.nonzero(sorted_ids != M)[0]
+    routes = (sorted_ids[real] & 0xFFFFFF).astype(np.int64) * w.topk + (sorted_ids[real] >> 24)
+    giq = iq.cpu().numpy()[real]
+    gis = is_.cpu().numpy()[real]
+    assert not (gis == 0xFF).any(), "unwritten scales in routed rows"
+    assert not (giq == 0xFF).any(), "unwritten codes in routed rows"
+    check_intermediate(L, hidden, ids, routes, giq, gis)
+    if w.inter_valid < w.inter:
+        assert np.all((giq[:, w.inter_valid:] & 0x7F) == 0)

@@ -159,3 +159,24 @@ def test_shared_expert_decomposes(oracle):
     _, o_routed = oracle.forward(hidden, ids[:, :-1], wts[:, :-1], w13, w13_s, w2, w2_s, want_f64=True)
     y_shared, _, _ = silu_mlp_dense(hidden, w13[8], w13_s[8], w2[8], w2_s[8])
     np.testing.assert_allclose(o_all, o_routed + y_shared, rtol=1e-12, atol=1e-12)
+
+
+def test_given_intermediate_reproduces_forward(oracle, inv_case):
+    """Stage two + combine on the oracle's own intermediate is the forward."""
+    w, (w13, w13_s, w2, w2_s), hidden, ids, wts = inv_case
+    out, o64 = oracle.forward(hidden, ids, wts, w13, w13_s, w2, w2_s, want_f64=True)
+    M, k = ids.shape
+    routes = np.arange(M * k, dtype=np.int64)
+    iq, is_ = oracle.intermediate(hidden, ids, w13, w13_s, routes)
+    out2, o2 = oracle.forward_given_intermediate(ids, wts, w2, w2_s, iq.reshape(M, k, -1),
+                                                 is_.reshape(M, k, -1), want_f64=True)
+    assert np.array_equal(out, out2) and np.array_equal(o64, o2)
+    # a changed intermediate element moves the output by exactly w * w2[:, j] * delta
+    iq2 = iq.copy()
+    iq2[0, 5] = (iq2[0, 5] + 1) % 0x7E
+    _, o3 = oracle.forward_given_intermediate(ids, wts, w2, w2_s, iq2.reshape(M, k, -1),
+                                              is_.reshape(M, k, -1), want_f64=True)
+    W2 = ind.dequant_mxfp4(w2[ids[0, 0]], w2_s[ids[0, 0]])
+    scale = ind.E8M0_ALL[is_[0, 0]]
+    delta = (ind.E4M3_ALL[iq2[0, 5]] - ind.E4M3_ALL[iq[0, 5]]) * scale
+    np.testing.assert_allclose(o3[0] - o64[0], float(wts[0, 0]) * W2[:, 5] * delta, rtol=1e-9, atol=1e-12)
