@@ -1,0 +1,244 @@
+"""Benchmark of the A8W4 fused-MoE layer on one MI355X.
+
+Workload: the backbone decode sweep -- hidden 5120, 384 experts, top-6,
+intermediate 576 zero-padded to 640, MXFP4 weights with E8M0 scales, BF16
+N(0,1) activations, softmax top-6 routing -- at the eight decode token
+buckets M = 6, 12, 24, 48, 96, 192, 384, 768 (aiter PR 5609, "Add DeepSeek
+V4.1 Flash TP4 gfx950 MoE tuning", Configuration).  All inputs are seeded
+synthetic data resident in HBM before timing starts.
+
+One step = one full call of the layer (activation quantisation, sort, stage
+one, stage two, BF16 output) for each of the eight buckets.  Each bucket
+reads its own copy of the packed weights, so every call streams its
+experts' weights from HBM rather than from the 256 MB last-level cache.
+
+Printed: one JSON line with the mean microseconds per call over the sweep,
+per-bucket microseconds / GB/s / TFLOP/s, the roofline position of the
+dominant kernel (stage one, timed with HIP events on its stream inside the
+timed loop), and the CPU oracle timed on a bounded sample as a baseline.
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0           # MI355X HBM3E, GB/s
+FP8_PEAK_TFLOPS = 5000.0        # dense MFMA, FP8 operands (the A operand here is FP8)
+FP4_PEAK_TFLOPS = 10100.0       # dense MFMA, FP4/FP6 operands
+BUCKETS = (6, 12, 24, 48, 96, 192, 384, 768)
+METRIC = "fused-MoE µs/call per token bucket; HBM GB/s (decode) / MFMA util (prefill)"
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--cpu-seconds", type=float, default=15.0,
+                    help="target CPU time of the oracle baseline sample")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    return ap.parse_args()
+
+
+def algorithmic(w, M, ids):
+    """Algorithmic bytes and flops of one call (and of its stage one)."""
+    H, I, k = w.hidden, w.inter, w.topk
+    le = ids.astype(np.int64) - w.expert_offset
+    local = (le >= 0) & (le < w.num_experts)
+    R = int(local.sum())
+    D = int(np.unique(le[local]).size)
+    w13 = 2 * I * (H // 2 + H // 32)            # gate/up codes + scales of one expert
+    w2 = H * (I // 2 + I // 32)
+    act = M * (H + H // 32)                      # FP8 activations + scales
+    inter = R * (I + I // 32)                    # requantised intermediate
+    call = D * (w13 + w2) + M * H * 2 + M * k * 8 + 2 * act + 2 * inter + M * H * 2
+    s1 = D * w13 + act + inter
+    flops = 6.0 * R * I * H
+    return dict(R=R, D=D, bytes=call, stage1_bytes=s1, flops=flops, stage1_flops=4.0 * R * I * H)
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print("bench.py runs on one GPU: this build has no multi-GPU path "
+              "(the layer is measured on one GPU's share of the experts).", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from mixture_experts_fp8_amd import abi, workloads as wl
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    dev = torch.device("cuda:0")
+    lib = abi.load()
+    w = wl.WORKLOADS["backbone-decode"]
+
+    # ---- weights: generated once, packed, one device copy per bucket
+    t0 = time.time()
+    host_w = wl.make_weights(w)
+    d1 = abi.make_dims(1, w.hidden, w.inter, w.num_experts, w.topk, w.expert_offset)
+    raw = [torch.from_numpy(np.ascontiguousarray(x)).to(dev) for x in host_w]
+    packed0 = abi.moe_a8w4_pack_weights(d1, *raw)
+    del raw
+    copies = [packed0] + [tuple(t.clone() for t in packed0) for _ in BUCKETS[1:]]
+    torch.cuda.synchronize()
+    print("setup: weights generated, packed and copied in %.1f s" % (time.time() - t0),
+          file=sys.stderr, flush=True)
+
+    stream = torch.cuda.current_stream()
+    sp = ctypes.c_void_p(stream.cuda_stream)
+    vp = lambda t: ctypes.c_void_p(t.data_ptr())
+
+    # ---- per-bucket resident inputs, outputs, workspace and prebuilt call arguments
+    buckets = []
+    for bi, M in enumerate(BUCKETS):
+        hidden, ids, wts = wl.make_inputs(w, M, "softmax")
+        d = abi.make_dims(M, w.hidden, w.inter, w.num_experts, w.topk, w.expert_offset)
+        bm = abi.moe_a8w4_block_m(d)
+        cap = abi.moe_a8w4_sort_capacity(d, bm)
+        b = dict(M=M, bm=bm, dims=d, ids=ids, alg=algorithmic(w, M, ids))
+        b["x"] = torch.from_numpy(hidden.view(np.int16)).to(dev).view(torch.bfloat16)
+        b["idd"] = torch.from_numpy(ids).to(dev)
+        b["wd"] = torch.from_numpy(wts).to(dev)
+        b["out"] = torch.empty((M, w.hidden), dtype=torch.bfloat16, device=dev)
+        b["ws"] = torch.empty(abi.moe_a8w4_workspace_bytes(d), dtype=torch.uint8, device=dev)
+        b["aq"] = torch.empty((M, w.hidden), dtype=torch.uint8, device=dev)
+        b["as"] = torch.empty((M, w.hidden // 32), dtype=torch.uint8, device=dev)
+        b["y"] = torch.empty((M, w.topk, w.hidden), dtype=torch.float32, device=dev)
+        b["srt"] = torch.empty(cap, dtype=torch.int32, device=dev)
+        b["bexp"] = torch.empty(cap // bm, dtype=torch.int32, device=dev)
+        b["npad"] = torch.empty(1, dtype=torch.int32, device=dev)
+        b["iq"] = torch.empty((cap, w.inter), dtype=torch.uint8, device=dev)
+        b["is"] = torch.empty((cap, w.inter // 32), dtype=torch.uint8, device=dev)
+        p13, p13s, p2, p2s = copies[bi]
+        dref = ctypes.byref(d)
+        b["a_quant"] = (ctypes.c_int32(M), ctypes.c_int32(w.hidden), vp(b["x"]), vp(b["aq"]),
+                        vp(b["as"]), sp)
+        b["a_sort"] = (dref, ctypes.c_int32(bm), vp(b["idd"]), vp(b["srt"]), vp(b["bexp"]),
+                       vp(b["npad"]), sp)
+        b["a_s1"] = (dref, ctypes.c_int32(bm), vp(b["aq"]), vp(b["as"]), vp(b["srt"]), vp(b["bexp"]),
+                     vp(b["npad"]), vp(p13), vp(p13s), vp(b["iq"]), vp(b["is"]), sp)
+        b["a_s2"] = (dref, ctypes.c_int32(bm), vp(b["iq"]), vp(b["is"]), vp(b["srt"]), vp(b["bexp"]),
+                     vp(b["npad"]), vp(b["wd"]), vp(p2), vp(p2s), vp(b["y"]), sp)
+        b["a_fin"] = (dref, vp(b["idd"]), vp(b["y"]), vp(b["out"]), sp)
+        b["a_fwd"] = (dref, vp(b["x"]), vp(b["idd"]), vp(b["wd"]), vp(p13), vp(p13s), vp(p2), vp(p2s),
+                      vp(b["out"]), vp(b["ws"]), ctypes.c_size_t(b["ws"].numel()), sp)
+        buckets.append(b)
+    torch.cuda.synchronize()
+
+    f_quant, f_sort, f_s1 = lib.moe_a8w4_quant_act, lib.moe_a8w4_sort, lib.moe_a8w4_stage1
+    f_s2, f_fin, f_fwd = lib.moe_a8w4_stage2, lib.moe_a8w4_combine, lib.moe_a8w4_forward
+
+    def call(b, ev=None):
+        """One layer call through the step entry points; stage one between events."""
+        st = f_quant(*b["a_quant"]) | f_sort(*b["a_sort"])
+        if ev is not None:
+            ev[0].record(stream)
+        st |= f_s1(*b["a_s1"])
+        if ev is not None:
+            ev[1].record(stream)
+        st |= f_s2(*b["a_s2"]) | f_fin(*b["a_fin"])
+        if st:
+            raise RuntimeError("layer call failed with status %d" % st)
+
+    for _ in range(args.warmup):
+        for b in buckets:
+            call(b)
+    torch.cuda.synchronize()
+
+    # ---- timed region: K steps, stage one bracketed by events on its stream
+    K = args.steps
+    events = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in buckets] for _ in range(K)]
+    torch.cuda.synchronize()
+    t_start = time.perf_counter()
+    for s in range(K):
+        for bi, b in enumerate(buckets):
+            call(b, events[s][bi])
+    torch.cuda.synchronize()
+    t_end = time.perf_counter()
+    ms_per_step = (t_end - t_start) * 1e3 / K
+    s1_us = np.array([[events[s][bi][0].elapsed_time(events[s][bi][1]) * 1e3 for bi in range(len(buckets))]
+                      for s in range(K)])
+
+    # ---- per-bucket call time through the single forward entry point
+    reps = max(5, K)
+    per_bucket = {}
+    for bi, b in enumerate(buckets):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        ts = []
+        for r in range(reps):
+            # another bucket's call in between keeps this bucket's weights out of cache
+            call(buckets[(bi + 4) % len(buckets)])
+            e0.record(stream)
+            if f_fwd(*b["a_fwd"]):
+                raise RuntimeError("moe_a8w4_forward failed")
+            e1.record(stream)
+            e1.synchronize()
+            ts.append(e0.elapsed_time(e1) * 1e3)
+        us = float(np.median(ts))
+        a = b["alg"]
+        s1 = float(np.mean(s1_us[:, bi]))
+        per_bucket[str(b["M"])] = dict(
+            us_per_call=round(us, 2), routes=a["R"], experts_touched=a["D"], block_m=b["bm"],
+            GBps=round(a["bytes"] / us / 1e3, 1), hbm_frac=round(a["bytes"] / us / 1e3 / HBM_PEAK_GBS, 4),
+            TFLOPs=round(a["flops"] / us / 1e6, 2), stage1_us=round(s1, 2),
+            stage1_GBps=round(a["stage1_bytes"] / s1 / 1e3, 1))
+
+    # ---- roofline of the dominant kernel (stage one), from the timed loop
+    s1_bytes = sum(b["alg"]["stage1_bytes"] for b in buckets)
+    s1_time = float(s1_us.mean(axis=0).sum())
+    achieved = s1_bytes / s1_time / 1e3
+    roofline = dict(bound="hbm", achieved=round(achieved, 1), peak=HBM_PEAK_GBS, unit="GB/s",
+                    frac=round(achieved / HBM_PEAK_GBS, 4), traffic=None,
+                    kernel="stage-one grouped GEMM (gemm_kernel<1,*,4>)",
+                    bytes_per_launch_mean=round(s1_bytes / len(buckets)),
+                    launch_us_mean=round(s1_time / len(buckets), 2))
+
+    value = ms_per_step * 1e3 / len(buckets)
+    result = {
+        "metric": METRIC, "value": round(value, 2), "unit": "us/call", "n_gpus": 1,
+        "steps": K, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": False, "scaling": "weak", "vs_baseline": None,
+        "dtype": "f8e4m3 x f4e2m1 -> f32", "data": "synthetic",
+        "config": {"workload": "backbone decode sweep: H5120, 384 experts, top-6, "
+                               "I 576 padded to 640, MXFP4 weights, softmax routing",
+                   "tokens": list(BUCKETS), "value": "mean us per call over the eight buckets"},
+        "buckets": per_bucket, "roofline": roofline,
+    }
+
+    # ---- CPU baseline: the oracle on a bounded sample of the same workload
+    if not args.no_cpu_baseline:
+        import oracle
+        b = buckets[-1]
+        hidden = b["x"].view(torch.int16).cpu().numpy().view(np.uint16)
+        wts = b["wd"].cpu().numpy()
+        rng = np.random.default_rng(0)
+        n = 4
+        t = time.perf_counter()
+        oracle.forward(hidden, b["ids"], wts, *host_w, tokens=rng.choice(b["M"], n, replace=False))
+        dt = time.perf_counter() - t
+        n2 = int(min(b["M"], max(n, n * args.cpu_seconds / max(dt, 1e-3))))
+        tok = rng.choice(b["M"], n2, replace=False)
+        t = time.perf_counter()
+        oracle.forward(hidden, b["ids"], wts, *host_w, tokens=tok)
+        dt = time.perf_counter() - t
+        per_route = dt / (n2 * w.topk)
+        mean_us = float(np.mean([bb["alg"]["R"] * per_route * 1e6 for bb in buckets]))
+        result["cpu_baseline"] = dict(
+            value=round(mean_us, 1), unit="us/call", cores=oracle.num_threads(), kind="oracle",
+            sample="%d tokens (%d routes) of the M=768 bucket in %.1f s, scaled by each bucket's "
+                   "routes; mean over the eight buckets" % (n2, n2 * w.topk, dt))
+    print(json.dumps(result))
+
+
+if __name__ == "__main__":
+    main()

@@ -113,9 +113,8 @@ int moe_a8w4_forward(const moe_a8w4_dims* dims, const void* hidden, const int32_
 /* ----------------------------------------------- the steps, one at a time */
 
 /* Per-1x32 FP8 quantisation of BF16 rows: x [M, H] -> q [M, H] E4M3 codes,
- * s [M, H/32] E8M0 codes.  If zero_f32 is not NULL, [M, H] floats there are
- * set to 0 (the combine buffer of stage two).  H must be a multiple of 32. */
-int moe_a8w4_quant_act(int32_t M, int32_t H, const void* x, uint8_t* q, uint8_t* s, float* zero_f32,
+ * s [M, H/32] E8M0 codes.  H must be a multiple of 32. */
+int moe_a8w4_quant_act(int32_t M, int32_t H, const void* x, uint8_t* q, uint8_t* s,
                        hipStream_t stream);
 
 /* Group local routes by expert: sorted_ids [capacity] receives, expert by
@@ -138,15 +137,20 @@ int moe_a8w4_stage1(const moe_a8w4_dims* dims, int32_t block_m, const uint8_t* a
                     const int32_t* num_padded, const uint8_t* w13_p, const uint8_t* w13_s_p,
                     uint8_t* inter_q, uint8_t* inter_s, hipStream_t stream);
 
-/* Stage two: adds topk_weights[t,k] * (w2[e] h) of every route into
- * acc [M, H] float32 (which must hold zeros, or a partial sum, beforehand). */
+/* Stage two: for every local route (t, k), y_routes[t, k, :] (float32,
+ * [M, topk, H]) receives topk_weights[t,k] * (w2[e] h), h its dequantised
+ * intermediate.  Rows of non-local slots are not written. */
 int moe_a8w4_stage2(const moe_a8w4_dims* dims, int32_t block_m, const uint8_t* inter_q,
                     const uint8_t* inter_s, const int32_t* sorted_ids, const int32_t* block_expert,
                     const int32_t* num_padded, const float* topk_weights, const uint8_t* w2_p,
-                    const uint8_t* w2_s_p, float* acc, hipStream_t stream);
+                    const uint8_t* w2_s_p, float* y_routes, hipStream_t stream);
 
-/* acc [M, H] float32 -> out [M, H] BF16, round to nearest even. */
-int moe_a8w4_finalize(int32_t M, int32_t H, const float* acc, void* out, hipStream_t stream);
+/* Top-k combine: out[t, :] (BF16, [M, H]) = round-to-nearest-even of the
+ * float32 sum, in ascending k, of y_routes[t, k, :] over the token's local
+ * slots (topk_ids decides which slots are local); zero for a token without
+ * one.  Bitwise repeatable. */
+int moe_a8w4_combine(const moe_a8w4_dims* dims, const int32_t* topk_ids, const float* y_routes,
+                     void* out, hipStream_t stream);
 
 /* Name of a status code (static string). */
 const char* moe_a8w4_status_str(int status);

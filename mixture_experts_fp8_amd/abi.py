@@ -26,7 +26,7 @@ MOE_ERR_BLOCK_M = -5
 EXPORTS = (
     "moe_a8w4_workspace_bytes", "moe_a8w4_block_m", "moe_a8w4_sort_capacity",
     "moe_a8w4_pack_weights", "moe_a8w4_forward", "moe_a8w4_quant_act", "moe_a8w4_sort",
-    "moe_a8w4_stage1", "moe_a8w4_stage2", "moe_a8w4_finalize", "moe_a8w4_status_str",
+    "moe_a8w4_stage1", "moe_a8w4_stage2", "moe_a8w4_combine", "moe_a8w4_status_str",
 )
 
 
@@ -64,11 +64,11 @@ def load() -> ctypes.CDLL:
         "moe_a8w4_sort_capacity": (ctypes.c_int64, [P, i32]),
         "moe_a8w4_pack_weights": (ctypes.c_int, [P] + [vp] * 8 + [vp]),
         "moe_a8w4_forward": (ctypes.c_int, [P] + [vp] * 9 + [sz, vp]),
-        "moe_a8w4_quant_act": (ctypes.c_int, [i32, i32, vp, vp, vp, vp, vp]),
+        "moe_a8w4_quant_act": (ctypes.c_int, [i32, i32, vp, vp, vp, vp]),
         "moe_a8w4_sort": (ctypes.c_int, [P, i32, vp, vp, vp, vp, vp]),
         "moe_a8w4_stage1": (ctypes.c_int, [P, i32] + [vp] * 9 + [vp]),
         "moe_a8w4_stage2": (ctypes.c_int, [P, i32] + [vp] * 9 + [vp]),
-        "moe_a8w4_finalize": (ctypes.c_int, [i32, i32, vp, vp, vp]),
+        "moe_a8w4_combine": (ctypes.c_int, [P, vp, vp, vp, vp]),
         "moe_a8w4_status_str": (ctypes.c_char_p, [ctypes.c_int]),
     }
     for name, (res, args) in sig.items():
@@ -149,13 +149,13 @@ def moe_a8w4_forward(dims, hidden, topk_ids, topk_weights, w13_p, w13_s_p, w2_p,
 
 # ------------------------------------------------------------- the steps
 
-def moe_a8w4_quant_act(x, q=None, s=None, zero_f32=None, stream=None):
+def moe_a8w4_quant_act(x, q=None, s=None, stream=None):
     M, H = x.shape
     if q is None:
         q = torch.empty((M, H), dtype=torch.uint8, device=x.device)
     if s is None:
         s = torch.empty((M, H // 32), dtype=torch.uint8, device=x.device)
-    st = load().moe_a8w4_quant_act(M, H, _ptr(x), _ptr(q), _ptr(s), _ptr(zero_f32), _stream(stream))
+    st = load().moe_a8w4_quant_act(M, H, _ptr(x), _ptr(q), _ptr(s), _stream(stream))
     _check("moe_a8w4_quant_act", st)
     return q, s
 
@@ -192,19 +192,22 @@ def moe_a8w4_stage1(dims, block_m, a_q, a_s, sorted_ids, block_expert, num_padde
 
 
 def moe_a8w4_stage2(dims, block_m, inter_q, inter_s, sorted_ids, block_expert, num_padded,
-                    topk_weights, w2_p, w2_s_p, acc, stream=None):
+                    topk_weights, w2_p, w2_s_p, y_routes=None, stream=None):
+    if y_routes is None:
+        y_routes = torch.empty((dims.tokens, dims.topk, dims.hidden), dtype=torch.float32,
+                               device=inter_q.device)
     st = load().moe_a8w4_stage2(ctypes.byref(dims), block_m, _ptr(inter_q), _ptr(inter_s),
                                 _ptr(sorted_ids), _ptr(block_expert), _ptr(num_padded),
-                                _ptr(topk_weights), _ptr(w2_p), _ptr(w2_s_p), _ptr(acc),
+                                _ptr(topk_weights), _ptr(w2_p), _ptr(w2_s_p), _ptr(y_routes),
                                 _stream(stream))
     _check("moe_a8w4_stage2", st)
-    return acc
+    return y_routes
 
 
-def moe_a8w4_finalize(acc, out=None, stream=None):
-    M, H = acc.shape
+def moe_a8w4_combine(dims, topk_ids, y_routes, out=None, stream=None):
     if out is None:
-        out = torch.empty((M, H), dtype=torch.bfloat16, device=acc.device)
-    st = load().moe_a8w4_finalize(M, H, _ptr(acc), _ptr(out), _stream(stream))
-    _check("moe_a8w4_finalize", st)
+        out = torch.empty((dims.tokens, dims.hidden), dtype=torch.bfloat16, device=y_routes.device)
+    st = load().moe_a8w4_combine(ctypes.byref(dims), _ptr(topk_ids), _ptr(y_routes), _ptr(out),
+                                 _stream(stream))
+    _check("moe_a8w4_combine", st)
     return out

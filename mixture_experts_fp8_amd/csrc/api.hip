@@ -48,7 +48,7 @@ int64_t capacity(const moe_a8w4_dims* d, int bm) {
 }
 
 struct Layout {
-  size_t aq, as, sorted, bexp, npad, iq, is, acc, total;
+  size_t aq, as, sorted, bexp, npad, iq, is, y, total;
 };
 
 size_t al256(size_t x) { return (x + 255) & ~(size_t)255; }
@@ -65,7 +65,7 @@ Layout layout(const moe_a8w4_dims* d, int bm) {
   L.npad = o;   o += 256;
   L.iq = o;     o += al256(cap * I);
   L.is = o;     o += al256(cap * I / 32);
-  L.acc = o;    o += al256(M * H * 4);
+  L.y = o;      o += al256(M * (size_t)d->topk * H * 4);
   L.total = o;
   return L;
 }
@@ -82,11 +82,11 @@ GemmArgs stage1_args(const moe_a8w4_dims* d, int bm, const uint8_t* a_q, const u
 
 GemmArgs stage2_args(const moe_a8w4_dims* d, int bm, const uint8_t* iq, const uint8_t* is,
                      const int32_t* sorted, const int32_t* bexp, const int32_t* npad,
-                     const float* wts, const uint8_t* w, const uint8_t* ws, float* acc) {
+                     const float* wts, const uint8_t* w, const uint8_t* ws, float* y) {
   GemmArgs a = {};
   a.M = d->tokens; a.topk = d->topk; a.N = d->hidden; a.K = d->inter; a.bm = bm;
   a.sorted_ids = sorted; a.block_expert = bexp; a.num_padded = npad;
-  a.bq = iq; a.bs = is; a.w = w; a.ws = ws; a.topk_weights = wts; a.acc = acc;
+  a.bq = iq; a.bs = is; a.w = w; a.ws = ws; a.topk_weights = wts; a.y_routes = y;
   return a;
 }
 
@@ -156,11 +156,11 @@ int moe_a8w4_forward(const moe_a8w4_dims* dims, const void* hidden, const int32_
   int32_t* npad = reinterpret_cast<int32_t*>(ws + L.npad);
   uint8_t* iq = ws + L.iq;
   uint8_t* is = ws + L.is;
-  float* acc = reinterpret_cast<float*>(ws + L.acc);
+  float* y = reinterpret_cast<float*>(ws + L.y);
   const int64_t max_blocks = capacity(dims, bm) / bm;
 
   hipError_t e = moe::launch_act_quant(dims->tokens, dims->hidden,
-                                       static_cast<const uint16_t*>(hidden), a_q, a_s, acc, stream);
+                                       static_cast<const uint16_t*>(hidden), a_q, a_s, stream);
   if (e != hipSuccess) return status_of(e);
   e = moe::launch_sort(topk_ids, dims->tokens, dims->topk, dims->num_experts, dims->expert_offset,
                        bm, sorted, bexp, npad, stream);
@@ -169,20 +169,20 @@ int moe_a8w4_forward(const moe_a8w4_dims* dims, const void* hidden, const int32_
                          max_blocks, stream);
   if (e != hipSuccess) return status_of(e);
   e = moe::launch_stage2(stage2_args(dims, bm, iq, is, sorted, bexp, npad, topk_weights, w2_p,
-                                     w2_s_p, acc), max_blocks, stream);
+                                     w2_s_p, y), max_blocks, stream);
   if (e != hipSuccess) return status_of(e);
-  return status_of(moe::launch_finalize(dims->tokens, dims->hidden, acc,
-                                        static_cast<uint16_t*>(out), stream));
+  return status_of(moe::launch_combine(dims->tokens, dims->hidden, dims->topk, dims->num_experts,
+                                       dims->expert_offset, topk_ids, y,
+                                       static_cast<uint16_t*>(out), stream));
 }
 
-int moe_a8w4_quant_act(int32_t M, int32_t H, const void* x, uint8_t* q, uint8_t* s, float* zero_f32,
+int moe_a8w4_quant_act(int32_t M, int32_t H, const void* x, uint8_t* q, uint8_t* s,
                        hipStream_t stream) {
   if (M < 0 || H <= 0 || H % 32 != 0) return MOE_ERR_DIMS;
   if (M == 0) return MOE_OK;
   if (!x || !q || !s) return MOE_ERR_NULL;
-  if (!aligned(x, 16) || !aligned(q, 16) || (zero_f32 && !aligned(zero_f32, 16)))
-    return MOE_ERR_ALIGN;
-  return status_of(moe::launch_act_quant(M, H, static_cast<const uint16_t*>(x), q, s, zero_f32, stream));
+  if (!aligned(x, 16) || !aligned(q, 16)) return MOE_ERR_ALIGN;
+  return status_of(moe::launch_act_quant(M, H, static_cast<const uint16_t*>(x), q, s, stream));
 }
 
 int moe_a8w4_sort(const moe_a8w4_dims* dims, int32_t block_m, const int32_t* topk_ids,
@@ -220,30 +220,34 @@ int moe_a8w4_stage1(const moe_a8w4_dims* dims, int32_t block_m, const uint8_t* a
 int moe_a8w4_stage2(const moe_a8w4_dims* dims, int32_t block_m, const uint8_t* inter_q,
                     const uint8_t* inter_s, const int32_t* sorted_ids, const int32_t* block_expert,
                     const int32_t* num_padded, const float* topk_weights, const uint8_t* w2_p,
-                    const uint8_t* w2_s_p, float* acc, hipStream_t stream) {
+                    const uint8_t* w2_s_p, float* y_routes, hipStream_t stream) {
   int st = check_dims(dims);
   if (st) return st;
   if (!valid_bm(block_m)) return MOE_ERR_BLOCK_M;
   if (dims->tokens == 0) return MOE_OK;
   const void* ptrs[10] = {inter_q, inter_s, sorted_ids, block_expert, num_padded, topk_weights,
-                          w2_p, w2_s_p, acc, inter_q};
+                          w2_p, w2_s_p, y_routes, inter_q};
   for (const void* p : ptrs)
     if (!p) return MOE_ERR_NULL;
-  if (!aligned(inter_q, 16) || !aligned(w2_p, 16) || !aligned(w2_s_p, 16) || !aligned(acc, 16))
+  if (!aligned(inter_q, 16) || !aligned(w2_p, 16) || !aligned(w2_s_p, 16) || !aligned(y_routes, 16))
     return MOE_ERR_ALIGN;
   const int64_t max_blocks = capacity(dims, block_m) / block_m;
   return status_of(moe::launch_stage2(stage2_args(dims, block_m, inter_q, inter_s, sorted_ids,
                                                   block_expert, num_padded, topk_weights, w2_p,
-                                                  w2_s_p, acc),
+                                                  w2_s_p, y_routes),
                                       max_blocks, stream));
 }
 
-int moe_a8w4_finalize(int32_t M, int32_t H, const float* acc, void* out, hipStream_t stream) {
-  if (M < 0 || H <= 0 || H % 8 != 0) return MOE_ERR_DIMS;
-  if (M == 0) return MOE_OK;
-  if (!acc || !out) return MOE_ERR_NULL;
-  if (!aligned(acc, 16) || !aligned(out, 16)) return MOE_ERR_ALIGN;
-  return status_of(moe::launch_finalize(M, H, acc, static_cast<uint16_t*>(out), stream));
+int moe_a8w4_combine(const moe_a8w4_dims* dims, const int32_t* topk_ids, const float* y_routes,
+                     void* out, hipStream_t stream) {
+  int st = check_dims(dims);
+  if (st) return st;
+  if (dims->tokens == 0) return MOE_OK;
+  if (!topk_ids || !y_routes || !out) return MOE_ERR_NULL;
+  if (!aligned(y_routes, 16) || !aligned(out, 16)) return MOE_ERR_ALIGN;
+  return status_of(moe::launch_combine(dims->tokens, dims->hidden, dims->topk, dims->num_experts,
+                                       dims->expert_offset, topk_ids, y_routes,
+                                       static_cast<uint16_t*>(out), stream));
 }
 
 const char* moe_a8w4_status_str(int status) {

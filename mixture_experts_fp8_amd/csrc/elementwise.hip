@@ -1,6 +1,6 @@
 // Bandwidth-bound kernels of the A8W4 MoE layer: the per-1x32 FP8 activation
-// quantiser (with the zero fill of the combine buffer folded in), the final
-// fp32 -> BF16 conversion, and the one-time MXFP4 weight packing.
+// quantiser, the top-k combine with the BF16 output conversion, and the
+// one-time MXFP4 weight packing.
 //
 // Activation quantisation: FP8 activations with one E8M0 scale per 1x32
 // block (aiter PR 5609, "Add DeepSeek V4.1 Flash TP4 gfx950 MoE tuning",
@@ -19,7 +19,6 @@ namespace {
 __global__ void __launch_bounds__(256) act_quant_kernel(const uint16_t* __restrict__ x,
                                                         uint8_t* __restrict__ q,
                                                         uint8_t* __restrict__ s,
-                                                        float* __restrict__ zero_acc,
                                                         int64_t n8) {
   const int64_t stride = (int64_t)gridDim.x * blockDim.x;
   for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n8; i += stride) {
@@ -39,26 +38,40 @@ __global__ void __launch_bounds__(256) act_quant_kernel(const uint16_t* __restri
     const uint2 codes = encode8(v, exp2_neg(E));
     *reinterpret_cast<uint2*>(q + i * 8) = codes;
     if ((i & 3) == 0) s[i >> 2] = (uint8_t)(E + 127);
-    if (zero_acc) {
-      float4* z = reinterpret_cast<float4*>(zero_acc + i * 8);
-      z[0] = make_float4(0.f, 0.f, 0.f, 0.f);
-      z[1] = make_float4(0.f, 0.f, 0.f, 0.f);
-    }
   }
 }
 
-__global__ void __launch_bounds__(256) finalize_kernel(const float* __restrict__ acc,
-                                                       uint16_t* __restrict__ out, int64_t n8) {
+// Top-k combine: out[t, h] = BF16( sum over the token's local slots k, in
+// ascending k, of y[t, k, h] ), y already holding topk_weight * (w2 h) of each
+// route in fp32 (the routing weight is applied after stage two: aiter PR
+// 5609, Configuration).  One thread per 8 consecutive outputs; slots whose
+// expert is not local were never written and are skipped, so a token with no
+// local route gets zeros.  The fixed summation order makes the result
+// bitwise repeatable.
+__global__ void __launch_bounds__(256) combine_kernel(const int32_t* __restrict__ ids,
+                                                      const float* __restrict__ y,
+                                                      uint16_t* __restrict__ out, int64_t n8,
+                                                      int H, int topk, int E, int expert_offset) {
   const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  const int h8 = H / 8;
   for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n8; i += stride) {
-    const float4 a = reinterpret_cast<const float4*>(acc + i * 8)[0];
-    const float4 b = reinterpret_cast<const float4*>(acc + i * 8)[1];
+    const int64_t t = i / h8;
+    const int h = (int)(i - t * h8) * 8;
+    float4 a = make_float4(0.f, 0.f, 0.f, 0.f), b = a;
+    for (int k = 0; k < topk; ++k) {
+      const int le = ids[t * topk + k] - expert_offset;
+      if ((unsigned)le >= (unsigned)E) continue;
+      const float4* src = reinterpret_cast<const float4*>(y + (t * topk + k) * H + h);
+      const float4 u = src[0], v = src[1];
+      a.x += u.x; a.y += u.y; a.z += u.z; a.w += u.w;
+      b.x += v.x; b.y += v.y; b.z += v.z; b.w += v.w;
+    }
     uint4 r;
     r.x = f32_to_bf16(a.x) | (f32_to_bf16(a.y) << 16);
     r.y = f32_to_bf16(a.z) | (f32_to_bf16(a.w) << 16);
     r.z = f32_to_bf16(b.x) | (f32_to_bf16(b.y) << 16);
     r.w = f32_to_bf16(b.z) | (f32_to_bf16(b.w) << 16);
-    *reinterpret_cast<uint4*>(out + i * 8) = r;
+    *reinterpret_cast<uint4*>(out + t * H + h) = r;
   }
 }
 
@@ -103,18 +116,19 @@ int grid_for(int64_t work, int per_block) {
 }  // namespace
 
 hipError_t launch_act_quant(int64_t M, int64_t H, const uint16_t* x, uint8_t* q, uint8_t* s,
-                            float* zero_acc, hipStream_t stream) {
+                            hipStream_t stream) {
   const int64_t n8 = M * H / 8;
   if (n8 == 0) return hipSuccess;
-  hipLaunchKernelGGL(act_quant_kernel, dim3(grid_for(n8, 256)), dim3(256), 0, stream, x, q, s,
-                     zero_acc, n8);
+  hipLaunchKernelGGL(act_quant_kernel, dim3(grid_for(n8, 256)), dim3(256), 0, stream, x, q, s, n8);
   return hipGetLastError();
 }
 
-hipError_t launch_finalize(int64_t M, int64_t H, const float* acc, uint16_t* out, hipStream_t stream) {
+hipError_t launch_combine(int64_t M, int32_t H, int32_t topk, int32_t E, int32_t expert_offset,
+                          const int32_t* ids, const float* y, uint16_t* out, hipStream_t stream) {
   const int64_t n8 = M * H / 8;
   if (n8 == 0) return hipSuccess;
-  hipLaunchKernelGGL(finalize_kernel, dim3(grid_for(n8, 256)), dim3(256), 0, stream, acc, out, n8);
+  hipLaunchKernelGGL(combine_kernel, dim3(grid_for(n8, 256)), dim3(256), 0, stream, ids, y, out, n8,
+                     H, topk, E, expert_offset);
   return hipGetLastError();
 }
 

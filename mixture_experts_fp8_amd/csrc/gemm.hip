@@ -4,8 +4,8 @@
 // w13[e] (MXFP4, interleaved: row 2j gate j, row 2j+1 up j) times the routed
 // tokens' FP8 activations, SiLU(gate) * up, and per-1x32 FP8 requantisation of
 // the intermediate, with no routing weight.  Stage two: w2[e] times that
-// intermediate, scaled by the routing weight and summed over the token's
-// top-k slots.  (aiter PR 5609, "Add DeepSeek V4.1 Flash TP4 gfx950 MoE
+// intermediate, scaled by the routing weight, written per route (token, slot)
+// for the top-k combine.  (aiter PR 5609, "Add DeepSeek V4.1 Flash TP4 gfx950 MoE
 // tuning", Configuration: BF16 output, FP8 activations, MXFP4 weights,
 // per-1x32 scaling, interleaved gate/up, SiLU, no stage-one routing-weight
 // multiplication; aiter PR 5904, "Fused-MoE kernel, expert-parallel
@@ -198,18 +198,19 @@ __global__ void __launch_bounds__(256) gemm_kernel(GemmArgs args) {
       }
     }
   } else {
-    // lane (t16, g) holds output columns 64*grp + 16g + 4t + r of its route
+    // lane (t16, g) holds output columns 64*grp + 16g + 4t + r of its route:
+    // 16 consecutive floats, so the four lanes of a route write 256 B in a row
     const int H = N;
 #pragma unroll
     for (int c = 0; c < NCG; ++c) {
       if (c < nact && valid[c]) {
         const int tok = rid[c] & 0xFFFFFF, k = rid[c] >> kSentinelShift;
-        const float wt = args.topk_weights[(int64_t)tok * args.topk + k];
-        float* dst = args.acc + (int64_t)tok * H + grp * 64 + 16 * g;
+        const int64_t slot = (int64_t)tok * args.topk + k;
+        const float wt = args.topk_weights[slot];
+        float4* dst = reinterpret_cast<float4*>(args.y_routes + slot * H + grp * 64 + 16 * g);
 #pragma unroll
         for (int t = 0; t < 4; ++t)
-#pragma unroll
-          for (int r = 0; r < 4; ++r) unsafeAtomicAdd(dst + 4 * t + r, wt * acc[t][c][r]);
+          dst[t] = make_float4(wt * acc[t][c][0], wt * acc[t][c][1], wt * acc[t][c][2], wt * acc[t][c][3]);
       }
     }
   }

@@ -23,15 +23,16 @@ struct GemmArgs {
   uint8_t* out_q;         // stage 1: intermediate codes [P, N/2]
   uint8_t* out_s;         // stage 1: intermediate scales [P, N/64]
   const float* topk_weights;  // stage 2: [M, topk]
-  float* acc;             // stage 2: fp32 combine buffer [M, K_out = N]
+  float* y_routes;        // stage 2: weighted route outputs [M, topk, N] fp32
 };
 
 hipError_t launch_act_quant(int64_t M, int64_t H, const uint16_t* x, uint8_t* q, uint8_t* s,
-                            float* zero_acc, hipStream_t stream);
+                            hipStream_t stream);
 hipError_t launch_sort(const int32_t* ids, int32_t M, int32_t topk, int32_t E, int32_t expert_offset,
                        int32_t bm, int32_t* sorted_ids, int32_t* block_expert, int32_t* num_padded,
                        hipStream_t stream);
-hipError_t launch_finalize(int64_t M, int64_t H, const float* acc, uint16_t* out, hipStream_t stream);
+hipError_t launch_combine(int64_t M, int32_t H, int32_t topk, int32_t E, int32_t expert_offset,
+                          const int32_t* ids, const float* y, uint16_t* out, hipStream_t stream);
 hipError_t launch_pack(const uint8_t* src, const uint8_t* src_s, uint8_t* dst, uint8_t* dst_s,
                        int64_t E, int64_t N, int64_t K, hipStream_t stream);
 // max_blocks: upper bound of sorted blocks (grid size); kernels read the real count on device
