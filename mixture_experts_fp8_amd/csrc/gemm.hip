@@ -43,6 +43,14 @@ __device__ __forceinline__ v4f mfma_fp4_fp8(const v4i& a, const v8i& b, const v4
   return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a8, b, c, 4, 0, OPSEL, (int)sa, 0, (int)sb);
 }
 
+// Weight loads: non-temporal (streamed past the caches) when an expert's
+// weights are read once per call, cached when several blocks reuse them.
+template <bool NT, typename T>
+__device__ __forceinline__ T load_w(const uint8_t* p) {
+  if constexpr (NT) return __builtin_nontemporal_load(reinterpret_cast<const T*>(p));
+  else return *reinterpret_cast<const T*>(p);
+}
+
 template <int NCG>
 struct Frag {
   v4i a[4];        // weight codes, one 16-byte K block per tile
@@ -52,7 +60,11 @@ struct Frag {
   uint32_t sb[NCG];
 };
 
-template <int STAGE, int NCG, int NWK>
+// STAGE 1 or 2; NCG column groups of 16 tokens (block_m = 16 NCG); NWK waves
+// splitting K inside a workgroup (4 / NWK row groups per workgroup); PD steps
+// of loads in flight per wave (PD - 1 steps prefetched ahead of the MFMAs);
+// NT streams the weights with non-temporal loads.
+template <int STAGE, int NCG, int NWK, int PD, bool NT>
 __global__ void __launch_bounds__(256) gemm_kernel(GemmArgs args) {
   constexpr int NWR = 4 / NWK;
   const int N = args.N, K = args.K, bm = args.bm, M = args.M;
@@ -104,8 +116,8 @@ __global__ void __launch_bounds__(256) gemm_kernel(GemmArgs args) {
   auto load = [&](Frag<NCG>& f, int s) {
     const uint8_t* w = wp + (int64_t)s * 4096;
 #pragma unroll
-    for (int t = 0; t < 4; ++t) f.a[t] = *reinterpret_cast<const v4i*>(w + t * 1024);
-    f.sa = *reinterpret_cast<const uint32_t*>(wsp + (int64_t)s * 256);
+    for (int t = 0; t < 4; ++t) f.a[t] = load_w<NT, v4i>(w + t * 1024);
+    f.sa = load_w<NT, uint32_t>(wsp + (int64_t)s * 256);
 #pragma unroll
     for (int c = 0; c < NCG; ++c) {
       if (c < nact) {
@@ -135,15 +147,19 @@ __global__ void __launch_bounds__(256) gemm_kernel(GemmArgs args) {
     }
   };
 
+  // software pipeline: a ring of PD fragments, loads issued PD - 1 steps ahead
   const int s0 = wk * (KS / NWK), s1 = s0 + KS / NWK;
-  Frag<NCG> f0, f1;
-  load(f0, s0);
-  for (int s = s0; s < s1; s += 2) {
-    if (s + 1 < s1) load(f1, s + 1);
-    compute(f0);
-    if (s + 1 >= s1) break;
-    if (s + 2 < s1) load(f0, s + 2);
-    compute(f1);
+  Frag<NCG> f[PD];
+#pragma unroll
+  for (int u = 0; u < PD - 1; ++u)
+    if (s0 + u < s1) load(f[u], s0 + u);
+  for (int s = s0; s < s1; s += PD) {
+#pragma unroll
+    for (int u = 0; u < PD; ++u) {
+      if (s + u >= s1) break;
+      if (s + u + PD - 1 < s1) load(f[(u + PD - 1) % PD], s + u + PD - 1);
+      compute(f[u]);
+    }
   }
 
   if constexpr (NWK > 1) {
@@ -216,34 +232,47 @@ __global__ void __launch_bounds__(256) gemm_kernel(GemmArgs args) {
   }
 }
 
-template <int STAGE, int NCG, int NWK>
+template <int STAGE, int NCG, int NWK, int PD, bool NT>
 hipError_t launch_gemm(const GemmArgs& a, int64_t max_blocks, hipStream_t stream) {
   constexpr int NWR = 4 / NWK;
   const int64_t NG = a.N / (NWR * 64);
   const int64_t grid = max_blocks * NG;
   if (grid <= 0) return hipSuccess;
-  hipLaunchKernelGGL((gemm_kernel<STAGE, NCG, NWK>), dim3((unsigned)grid), dim3(256), 0, stream, a);
+  hipLaunchKernelGGL((gemm_kernel<STAGE, NCG, NWK, PD, NT>), dim3((unsigned)grid), dim3(256), 0, stream, a);
   return hipGetLastError();
 }
+
+#ifndef MOE_S1_PD
+#define MOE_S1_PD 2
+#endif
+#ifndef MOE_S2_PD
+#define MOE_S2_PD 2
+#endif
+#ifndef MOE_S1_NWK_SMALL
+#define MOE_S1_NWK_SMALL 4
+#endif
+#ifndef MOE_NT_SMALL
+#define MOE_NT_SMALL true
+#endif
 
 }  // namespace
 
 hipError_t launch_stage1(const GemmArgs& a, int64_t max_blocks, hipStream_t stream) {
   switch (a.bm) {
-    case 16: return launch_gemm<1, 1, 4>(a, max_blocks, stream);
-    case 32: return launch_gemm<1, 2, 4>(a, max_blocks, stream);
-    case 64: return launch_gemm<1, 4, 1>(a, max_blocks, stream);
-    case 128: return launch_gemm<1, 8, 1>(a, max_blocks, stream);
+    case 16: return launch_gemm<1, 1, MOE_S1_NWK_SMALL, MOE_S1_PD, MOE_NT_SMALL>(a, max_blocks, stream);
+    case 32: return launch_gemm<1, 2, MOE_S1_NWK_SMALL, MOE_S1_PD, MOE_NT_SMALL>(a, max_blocks, stream);
+    case 64: return launch_gemm<1, 4, 1, 2, false>(a, max_blocks, stream);
+    case 128: return launch_gemm<1, 8, 1, 2, false>(a, max_blocks, stream);
     default: return hipErrorInvalidValue;
   }
 }
 
 hipError_t launch_stage2(const GemmArgs& a, int64_t max_blocks, hipStream_t stream) {
   switch (a.bm) {
-    case 16: return launch_gemm<2, 1, 1>(a, max_blocks, stream);
-    case 32: return launch_gemm<2, 2, 1>(a, max_blocks, stream);
-    case 64: return launch_gemm<2, 4, 1>(a, max_blocks, stream);
-    case 128: return launch_gemm<2, 8, 1>(a, max_blocks, stream);
+    case 16: return launch_gemm<2, 1, 1, MOE_S2_PD, MOE_NT_SMALL>(a, max_blocks, stream);
+    case 32: return launch_gemm<2, 2, 1, MOE_S2_PD, MOE_NT_SMALL>(a, max_blocks, stream);
+    case 64: return launch_gemm<2, 4, 1, 2, false>(a, max_blocks, stream);
+    case 128: return launch_gemm<2, 8, 1, 2, false>(a, max_blocks, stream);
     default: return hipErrorInvalidValue;
   }
 }
