@@ -122,10 +122,18 @@ int moe_a8w4_quant_act(int32_t M, int32_t H, const void* x, uint8_t* q, uint8_t*
  * as (k << 24) | t, each expert's run padded with M to a multiple of block_m
  * (experts without routes get no rows); block_expert [capacity/block_m]
  * receives the local expert of each block; num_padded [1] the total rows.
- * Entries past num_padded are left unspecified. */
+ * Entries past num_padded are left unspecified.  One workgroup sorts;
+ * the result does not depend on timing (bitwise repeatable). */
 int moe_a8w4_sort(const moe_a8w4_dims* dims, int32_t block_m, const int32_t* topk_ids,
                   int32_t* sorted_ids, int32_t* block_expert, int32_t* num_padded,
                   hipStream_t stream);
+
+/* moe_a8w4_quant_act and moe_a8w4_sort of one call in a single launch (the
+ * sort runs in one workgroup beside the quantiser): the first step of
+ * moe_a8w4_forward.  Same buffers and contracts as the two calls. */
+int moe_a8w4_quant_sort(const moe_a8w4_dims* dims, int32_t block_m, const void* hidden,
+                        const int32_t* topk_ids, uint8_t* a_q, uint8_t* a_s, int32_t* sorted_ids,
+                        int32_t* block_expert, int32_t* num_padded, hipStream_t stream);
 
 /* Stage one for every sorted block: inter_q [capacity, I] E4M3 codes and
  * inter_s [capacity, I/32] E8M0 codes, row p = sorted position, holding the

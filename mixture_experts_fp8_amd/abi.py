@@ -26,6 +26,7 @@ MOE_ERR_BLOCK_M = -5
 EXPORTS = (
     "moe_a8w4_workspace_bytes", "moe_a8w4_block_m", "moe_a8w4_sort_capacity",
     "moe_a8w4_pack_weights", "moe_a8w4_forward", "moe_a8w4_quant_act", "moe_a8w4_sort",
+    "moe_a8w4_quant_sort",
     "moe_a8w4_stage1", "moe_a8w4_stage2", "moe_a8w4_combine", "moe_a8w4_status_str",
 )
 
@@ -66,6 +67,7 @@ def load() -> ctypes.CDLL:
         "moe_a8w4_forward": (ctypes.c_int, [P] + [vp] * 9 + [sz, vp]),
         "moe_a8w4_quant_act": (ctypes.c_int, [i32, i32, vp, vp, vp, vp]),
         "moe_a8w4_sort": (ctypes.c_int, [P, i32, vp, vp, vp, vp, vp]),
+        "moe_a8w4_quant_sort": (ctypes.c_int, [P, i32] + [vp] * 7 + [vp]),
         "moe_a8w4_stage1": (ctypes.c_int, [P, i32] + [vp] * 9 + [vp]),
         "moe_a8w4_stage2": (ctypes.c_int, [P, i32] + [vp] * 9 + [vp]),
         "moe_a8w4_combine": (ctypes.c_int, [P, vp, vp, vp, vp]),
@@ -174,6 +176,23 @@ def moe_a8w4_sort(dims, block_m, topk_ids, sorted_ids=None, block_expert=None, n
                               _ptr(block_expert), _ptr(num_padded), _stream(stream))
     _check("moe_a8w4_sort", st)
     return sorted_ids, block_expert, num_padded
+
+
+def moe_a8w4_quant_sort(dims, block_m, hidden, topk_ids, stream=None):
+    """(a_q, a_s, sorted_ids, block_expert, num_padded) from one launch."""
+    cap = moe_a8w4_sort_capacity(dims, block_m)
+    dev = hidden.device
+    M, H = dims.tokens, dims.hidden
+    a_q = torch.empty((M, H), dtype=torch.uint8, device=dev)
+    a_s = torch.empty((M, H // 32), dtype=torch.uint8, device=dev)
+    sorted_ids = torch.empty(max(cap, 1), dtype=torch.int32, device=dev)
+    block_expert = torch.empty(max(cap // block_m, 1), dtype=torch.int32, device=dev)
+    num_padded = torch.empty(1, dtype=torch.int32, device=dev)
+    st = load().moe_a8w4_quant_sort(ctypes.byref(dims), block_m, _ptr(hidden), _ptr(topk_ids), _ptr(a_q),
+                                    _ptr(a_s), _ptr(sorted_ids), _ptr(block_expert), _ptr(num_padded),
+                                    _stream(stream))
+    _check("moe_a8w4_quant_sort", st)
+    return a_q, a_s, sorted_ids, block_expert, num_padded
 
 
 def moe_a8w4_stage1(dims, block_m, a_q, a_s, sorted_ids, block_expert, num_padded, w13_p, w13_s_p,

@@ -159,11 +159,9 @@ int moe_a8w4_forward(const moe_a8w4_dims* dims, const void* hidden, const int32_
   float* y = reinterpret_cast<float*>(ws + L.y);
   const int64_t max_blocks = capacity(dims, bm) / bm;
 
-  hipError_t e = moe::launch_act_quant(dims->tokens, dims->hidden,
-                                       static_cast<const uint16_t*>(hidden), a_q, a_s, stream);
-  if (e != hipSuccess) return status_of(e);
-  e = moe::launch_sort(topk_ids, dims->tokens, dims->topk, dims->num_experts, dims->expert_offset,
-                       bm, sorted, bexp, npad, stream);
+  hipError_t e = moe::launch_prep(topk_ids, dims->tokens, dims->topk, dims->num_experts,
+                                  dims->expert_offset, bm, sorted, bexp, npad,
+                                  static_cast<const uint16_t*>(hidden), dims->hidden, a_q, a_s, stream);
   if (e != hipSuccess) return status_of(e);
   e = moe::launch_stage1(stage1_args(dims, bm, a_q, a_s, sorted, bexp, npad, w13_p, w13_s_p, iq, is),
                          max_blocks, stream);
@@ -182,7 +180,8 @@ int moe_a8w4_quant_act(int32_t M, int32_t H, const void* x, uint8_t* q, uint8_t*
   if (M == 0) return MOE_OK;
   if (!x || !q || !s) return MOE_ERR_NULL;
   if (!aligned(x, 16) || !aligned(q, 16)) return MOE_ERR_ALIGN;
-  return status_of(moe::launch_act_quant(M, H, static_cast<const uint16_t*>(x), q, s, stream));
+  return status_of(moe::launch_prep(nullptr, M, 1, 1, 0, 16, nullptr, nullptr, nullptr,
+                                     static_cast<const uint16_t*>(x), H, q, s, stream));
 }
 
 int moe_a8w4_sort(const moe_a8w4_dims* dims, int32_t block_m, const int32_t* topk_ids,
@@ -193,9 +192,26 @@ int moe_a8w4_sort(const moe_a8w4_dims* dims, int32_t block_m, const int32_t* top
   if (!valid_bm(block_m)) return MOE_ERR_BLOCK_M;
   if (!num_padded) return MOE_ERR_NULL;
   if (dims->tokens > 0 && (!topk_ids || !sorted_ids || !block_expert)) return MOE_ERR_NULL;
-  return status_of(moe::launch_sort(topk_ids, dims->tokens, dims->topk, dims->num_experts,
+  return status_of(moe::launch_prep(topk_ids, dims->tokens, dims->topk, dims->num_experts,
                                     dims->expert_offset, block_m, sorted_ids, block_expert,
-                                    num_padded, stream));
+                                    num_padded, nullptr, 0, nullptr, nullptr, stream));
+}
+
+int moe_a8w4_quant_sort(const moe_a8w4_dims* dims, int32_t block_m, const void* hidden,
+                        const int32_t* topk_ids, uint8_t* a_q, uint8_t* a_s, int32_t* sorted_ids,
+                        int32_t* block_expert, int32_t* num_padded, hipStream_t stream) {
+  int st = check_dims(dims);
+  if (st) return st;
+  if (!valid_bm(block_m)) return MOE_ERR_BLOCK_M;
+  if (dims->tokens == 0) return MOE_OK;
+  const void* ptrs[7] = {hidden, topk_ids, a_q, a_s, sorted_ids, block_expert, num_padded};
+  for (const void* p : ptrs)
+    if (!p) return MOE_ERR_NULL;
+  if (!aligned(hidden, 16) || !aligned(a_q, 16)) return MOE_ERR_ALIGN;
+  return status_of(moe::launch_prep(topk_ids, dims->tokens, dims->topk, dims->num_experts,
+                                    dims->expert_offset, block_m, sorted_ids, block_expert,
+                                    num_padded, static_cast<const uint16_t*>(hidden), dims->hidden,
+                                    a_q, a_s, stream));
 }
 
 int moe_a8w4_stage1(const moe_a8w4_dims* dims, int32_t block_m, const uint8_t* a_q,

@@ -1,45 +1,11 @@
-// Bandwidth-bound kernels of the A8W4 MoE layer: the per-1x32 FP8 activation
-// quantiser, the top-k combine with the BF16 output conversion, and the
-// one-time MXFP4 weight packing.
-//
-// Activation quantisation: FP8 activations with one E8M0 scale per 1x32
-// block (aiter PR 5609, "Add DeepSeek V4.1 Flash TP4 gfx950 MoE tuning",
-// Configuration); the quantisation is part of the timed fused-MoE call (aiter
-// PR 5904, "Add tuned a8w4 fused-MoE configs for DeepSeek V4.1-Flash (TP4 + EP,
-// gfx950)", "Fused-MoE kernel, expert-parallel benchmark").
+// Bandwidth-bound kernels of the A8W4 MoE layer: the top-k combine with the
+// BF16 output conversion, and the one-time MXFP4 weight packing.
 #include "common.hpp"
 #include "launch.hpp"
 
 namespace moe {
 
 namespace {
-
-// Four lanes own one 32-element block: lane i of the quad loads 8 BF16 values
-// (16 B), so a wave reads 1 KB contiguous per load and writes 512 B of codes.
-__global__ void __launch_bounds__(256) act_quant_kernel(const uint16_t* __restrict__ x,
-                                                        uint8_t* __restrict__ q,
-                                                        uint8_t* __restrict__ s,
-                                                        int64_t n8) {
-  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
-  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n8; i += stride) {
-    // n8 is a multiple of 4 and the stride too, so a quad is either all in or all out
-    const uint4 raw = *reinterpret_cast<const uint4*>(x + i * 8);
-    float v[8];
-    v[0] = bf16_to_f32(raw.x & 0xFFFFu); v[1] = bf16_to_f32(raw.x >> 16);
-    v[2] = bf16_to_f32(raw.y & 0xFFFFu); v[3] = bf16_to_f32(raw.y >> 16);
-    v[4] = bf16_to_f32(raw.z & 0xFFFFu); v[5] = bf16_to_f32(raw.z >> 16);
-    v[6] = bf16_to_f32(raw.w & 0xFFFFu); v[7] = bf16_to_f32(raw.w >> 16);
-    float amax = 0.0f;
-#pragma unroll
-    for (int j = 0; j < 8; ++j) amax = fmaxf(amax, fabsf(v[j]));
-    amax = fmaxf(amax, __shfl_xor(amax, 1));
-    amax = fmaxf(amax, __shfl_xor(amax, 2));
-    const int E = block_exponent(amax);
-    const uint2 codes = encode8(v, exp2_neg(E));
-    *reinterpret_cast<uint2*>(q + i * 8) = codes;
-    if ((i & 3) == 0) s[i >> 2] = (uint8_t)(E + 127);
-  }
-}
 
 // Top-k combine: out[t, h] = BF16( sum over the token's local slots k, in
 // ascending k, of y[t, k, h] ), y already holding topk_weight * (w2 h) of each
@@ -114,14 +80,6 @@ int grid_for(int64_t work, int per_block) {
 }
 
 }  // namespace
-
-hipError_t launch_act_quant(int64_t M, int64_t H, const uint16_t* x, uint8_t* q, uint8_t* s,
-                            hipStream_t stream) {
-  const int64_t n8 = M * H / 8;
-  if (n8 == 0) return hipSuccess;
-  hipLaunchKernelGGL(act_quant_kernel, dim3(grid_for(n8, 256)), dim3(256), 0, stream, x, q, s, n8);
-  return hipGetLastError();
-}
 
 hipError_t launch_combine(int64_t M, int32_t H, int32_t topk, int32_t E, int32_t expert_offset,
                           const int32_t* ids, const float* y, uint16_t* out, hipStream_t stream) {

@@ -26,11 +26,11 @@ struct GemmArgs {
   float* y_routes;        // stage 2: weighted route outputs [M, topk, N] fp32
 };
 
-hipError_t launch_act_quant(int64_t M, int64_t H, const uint16_t* x, uint8_t* q, uint8_t* s,
-                            hipStream_t stream);
-hipError_t launch_sort(const int32_t* ids, int32_t M, int32_t topk, int32_t E, int32_t expert_offset,
+// One launch: workgroup 0 sorts the routes (skipped if ids is null), the
+// others quantise x [M, H] (skipped if x is null).
+hipError_t launch_prep(const int32_t* ids, int32_t M, int32_t topk, int32_t E, int32_t expert_offset,
                        int32_t bm, int32_t* sorted_ids, int32_t* block_expert, int32_t* num_padded,
-                       hipStream_t stream);
+                       const uint16_t* x, int64_t H, uint8_t* q, uint8_t* s, hipStream_t stream);
 hipError_t launch_combine(int64_t M, int32_t H, int32_t topk, int32_t E, int32_t expert_offset,
                           const int32_t* ids, const float* y, uint16_t* out, hipStream_t stream);
 hipError_t launch_pack(const uint8_t* src, const uint8_t* src_s, uint8_t* dst, uint8_t* dst_s,

@@ -100,6 +100,7 @@ def test_step_entry_points_validate():
     d = dims()
     p = ctypes.c_void_p(4096)
     assert lib.moe_a8w4_sort(ctypes.byref(d), 48, p, p, p, p, None) == abi.MOE_ERR_BLOCK_M
+    assert lib.moe_a8w4_quant_sort(ctypes.byref(d), 16, p, p, p, p, p, p, None, None) == abi.MOE_ERR_NULL
     assert lib.moe_a8w4_stage1(ctypes.byref(d), 16, *([p] * 8), None, None) == abi.MOE_ERR_NULL
     assert lib.moe_a8w4_stage2(ctypes.byref(d), 16, *([p] * 8), None, None) == abi.MOE_ERR_NULL
     assert lib.moe_a8w4_quant_act(4, 48, p, p, p, None) == abi.MOE_ERR_DIMS

@@ -135,7 +135,12 @@ def test_steps_compose_to_forward():
     out_steps = abi.moe_a8w4_combine(d, idd, y)
     out_fwd = layer.forward(xd, idd, wd)
     out_again = layer.forward(xd, idd, wd)
+    q2, s2, srt2, bexp2, npad2 = abi.moe_a8w4_quant_sort(d, bm, xd, idd)
     torch.cuda.synchronize()
+    P = int(npad.item())
+    assert int(npad2.item()) == P
+    assert torch.equal(q2, q) and torch.equal(s2, s)
+    assert torch.equal(srt2[:P], srt[:P]) and torch.equal(bexp2[:P // bm], bexp[:P // bm])
     # same kernels in the same order, no atomics: bitwise equal, and repeatable
     assert torch.equal(out_steps.view(torch.int16), out_fwd.view(torch.int16))
     assert torch.equal(out_again.view(torch.int16), out_fwd.view(torch.int16))
