@@ -48,7 +48,26 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="target CPU time of the oracle baseline sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="also run a 1 GiB device copy (reference for HBM byte counters)")
     return ap.parse_args()
+
+
+def measured_traffic():
+    """Stage-one HBM bytes per launch from the committed counter summary, or None
+    if the kernel sources changed since those counters were taken."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", "hbm_traffic_backbone_decode_sweep.md")
+    if not os.path.exists(path):
+        return None
+    for line in open(path):
+        if line.startswith("traffic-json: "):
+            rec = json.loads(line[len("traffic-json: "):])
+            h = hashlib.sha256()
+            for src in rec["sources"]:
+                h.update(open(os.path.join(ROOT, src), "rb").read())
+            return rec["bytes_per_launch"] if h.hexdigest() == rec["sources_sha256"] else None
+    return None
 
 
 def algorithmic(w, M, ids):
@@ -103,7 +122,7 @@ def main():
     buckets = []
     for bi, M in enumerate(BUCKETS):
         hidden, ids, wts = wl.make_inputs(w, M, "softmax")
-        d = abi.make_dims(M, w.hidden, w.inter, w.num_experts, w.topk, w.expert_offset)
+        d = abi.make_dims(M, w.hidden, w.inter, w.num_experts, w.topk, w.expert_offset, w.routed_experts)
         bm = abi.moe_a8w4_block_m(d)
         cap = abi.moe_a8w4_sort_capacity(d, bm)
         b = dict(M=M, bm=bm, dims=d, ids=ids, alg=algorithmic(w, M, ids))
@@ -198,7 +217,7 @@ def main():
     s1_time = float(s1_us.mean(axis=0).sum())
     achieved = s1_bytes / s1_time / 1e3
     roofline = dict(bound="hbm", achieved=round(achieved, 1), peak=HBM_PEAK_GBS, unit="GB/s",
-                    frac=round(achieved / HBM_PEAK_GBS, 4), traffic=None,
+                    frac=round(achieved / HBM_PEAK_GBS, 4), traffic=measured_traffic(),
                     kernel="stage-one grouped GEMM (gemm_kernel<1,*,4>)",
                     bytes_per_launch_mean=round(s1_bytes / len(buckets)),
                     launch_us_mean=round(s1_time / len(buckets), 2))
@@ -237,6 +256,14 @@ def main():
             value=round(mean_us, 1), unit="us/call", cores=oracle.num_threads(), kind="oracle",
             sample="%d tokens (%d routes) of the M=768 bucket in %.1f s, scaled by each bucket's "
                    "routes; mean over the eight buckets" % (n2, n2 * w.topk, dt))
+    if args.calibrate_copy:
+        # a plain copy of known size: 1 GiB read + 1 GiB written per launch
+        src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        result["calibration_copy_bytes"] = 1 << 30
     print(json.dumps(result))
 
 

@@ -63,6 +63,8 @@ typedef struct moe_a8w4_dims {
   int32_t num_experts;   /* E: experts held in the weight tensors */
   int32_t expert_offset; /* global id of weight expert 0 (a rank's local-expert slice) */
   int32_t topk;          /* slots per token */
+  int32_t routed_experts;/* experts the router chooses among, if more than num_experts
+                            (a local slice); 0 = num_experts.  Only sizes the blocks. */
 } moe_a8w4_dims;
 
 /* ------------------------------------------------------------------ sizes */
@@ -72,8 +74,9 @@ typedef struct moe_a8w4_dims {
 int moe_a8w4_workspace_bytes(const moe_a8w4_dims* dims, size_t* bytes);
 
 /* Rows per sorted block (16, 32, 64 or 128) that moe_a8w4_forward uses for
- * these dims; a function of M, topk and E only.  Negative status if invalid.
- * The same block_m is shared by the sort and both stages. */
+ * these dims: a function of the mean routes per expert,
+ * M * topk / max(num_experts, routed_experts), only.  Negative status if
+ * invalid.  The same block_m is shared by the sort and both stages. */
 int moe_a8w4_block_m(const moe_a8w4_dims* dims);
 
 /* Capacity, in entries, that sorted_ids needs for these dims and block_m:

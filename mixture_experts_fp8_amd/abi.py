@@ -34,11 +34,12 @@ EXPORTS = (
 class moe_a8w4_dims(ctypes.Structure):
     _fields_ = [("tokens", ctypes.c_int32), ("hidden", ctypes.c_int32), ("inter", ctypes.c_int32),
                 ("num_experts", ctypes.c_int32), ("expert_offset", ctypes.c_int32),
-                ("topk", ctypes.c_int32)]
+                ("topk", ctypes.c_int32), ("routed_experts", ctypes.c_int32)]
 
 
-def make_dims(tokens, hidden, inter, num_experts, topk, expert_offset=0) -> moe_a8w4_dims:
-    return moe_a8w4_dims(tokens, hidden, inter, num_experts, expert_offset, topk)
+def make_dims(tokens, hidden, inter, num_experts, topk, expert_offset=0,
+              routed_experts=0) -> moe_a8w4_dims:
+    return moe_a8w4_dims(tokens, hidden, inter, num_experts, expert_offset, topk, routed_experts)
 
 
 class MoeError(RuntimeError):

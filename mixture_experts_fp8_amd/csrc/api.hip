@@ -19,6 +19,7 @@ int check_dims(const moe_a8w4_dims* d) {
   if (d->inter <= 0 || d->inter % 128 != 0 || d->inter > (1 << 20)) return MOE_ERR_DIMS;
   if (d->num_experts < 1 || d->num_experts > moe::kMaxExperts) return MOE_ERR_DIMS;
   if (d->topk < 1 || d->topk > moe::kMaxTopk) return MOE_ERR_DIMS;
+  if (d->routed_experts < 0) return MOE_ERR_DIMS;
   return MOE_OK;
 }
 
@@ -28,15 +29,17 @@ int status_of(hipError_t e) { return e == hipSuccess ? MOE_OK : (int)e; }
 
 bool valid_bm(int bm) { return bm == 16 || bm == 32 || bm == 64 || bm == 128; }
 
-// Rows per sorted block from the mean number of routes per expert.  Column
-// groups of 16 past a block's last route are skipped by the GEMMs, so a larger
-// block only costs padding; a smaller one re-reads an expert's weights once
-// per extra block.
+// Rows per sorted block from the mean number of routes per expert (for a
+// local slice of experts, over all the experts the router chooses among).
+// Column groups of 16 past a block's last route are skipped by the GEMMs, so
+// a larger block only costs padding; a smaller one re-reads an expert's
+// weights once per extra block.
 int choose_bm(const moe_a8w4_dims* d) {
-  const double avg = (double)d->tokens * d->topk / d->num_experts;
+  const int experts = d->routed_experts > d->num_experts ? d->routed_experts : d->num_experts;
+  const double avg = (double)d->tokens * d->topk / experts;
   if (avg <= 8.0) return 16;
   if (avg <= 24.0) return 32;
-  if (avg <= 48.0) return 64;
+  if (avg <= 64.0) return 64;
   return 128;
 }
 

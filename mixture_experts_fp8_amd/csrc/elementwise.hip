@@ -13,7 +13,9 @@ namespace {
 // 5609, Configuration).  One thread per 8 consecutive outputs; slots whose
 // expert is not local were never written and are skipped, so a token with no
 // local route gets zeros.  The fixed summation order makes the result
-// bitwise repeatable.
+// bitwise repeatable.  H / 8 is a multiple of 64, so the 64 lanes of a wave
+// share one token: its slot mask is uniform, and all of the token's slot
+// loads are issued before the first add.
 __global__ void __launch_bounds__(256) combine_kernel(const int32_t* __restrict__ ids,
                                                       const float* __restrict__ y,
                                                       uint16_t* __restrict__ out, int64_t n8,
@@ -21,16 +23,28 @@ __global__ void __launch_bounds__(256) combine_kernel(const int32_t* __restrict_
   const int64_t stride = (int64_t)gridDim.x * blockDim.x;
   const int h8 = H / 8;
   for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n8; i += stride) {
-    const int64_t t = i / h8;
+    const int64_t t = __builtin_amdgcn_readfirstlane((int)(i / h8));
     const int h = (int)(i - t * h8) * 8;
-    float4 a = make_float4(0.f, 0.f, 0.f, 0.f), b = a;
-    for (int k = 0; k < topk; ++k) {
-      const int le = ids[t * topk + k] - expert_offset;
-      if ((unsigned)le >= (unsigned)E) continue;
-      const float4* src = reinterpret_cast<const float4*>(y + (t * topk + k) * H + h);
-      const float4 u = src[0], v = src[1];
-      a.x += u.x; a.y += u.y; a.z += u.z; a.w += u.w;
-      b.x += v.x; b.y += v.y; b.z += v.z; b.w += v.w;
+    unsigned mask = 0;
+#pragma unroll
+    for (int k = 0; k < kMaxTopk; ++k)
+      if (k < topk && (unsigned)(ids[t * topk + k] - expert_offset) < (unsigned)E) mask |= 1u << k;
+    v4f u[kMaxTopk], v[kMaxTopk];
+#pragma unroll
+    for (int k = 0; k < kMaxTopk; ++k) {
+      if (mask & (1u << k)) {
+        const v4f* src = reinterpret_cast<const v4f*>(y + (t * topk + k) * H + h);
+        u[k] = __builtin_nontemporal_load(src);
+        v[k] = __builtin_nontemporal_load(src + 1);
+      }
+    }
+    v4f a = {0.f, 0.f, 0.f, 0.f}, b = a;
+#pragma unroll
+    for (int k = 0; k < kMaxTopk; ++k) {
+      if (mask & (1u << k)) {
+        a += u[k];
+        b += v[k];
+      }
     }
     uint4 r;
     r.x = f32_to_bf16(a.x) | (f32_to_bf16(a.y) << 16);

@@ -1,4 +1,5 @@
-// Grouped GEMMs of the A8W4 MoE layer on the gfx950 scaled F8F6F4 MFMA.
+// Grouped GEMMs of the A8W4 MoE layer on the gfx950 scaled F8F6F4 MFMA, for
+// decode-sized blocks (block_m 16 .. 64); larger blocks use gemm_tile.hip.
 //
 // Stage one: for each block of sorted routes of expert e, gate/up rows of
 // w13[e] (MXFP4, interleaved: row 2j gate j, row 2j+1 up j) times the routed
@@ -21,27 +22,11 @@
 // the weights stream once.  A workgroup is 4 waves: either 4 row groups over
 // the whole K, or (small token counts) one row group with K split 4 ways and
 // the partial sums added through LDS in a fixed order.
-//
-// Operand layout of v_mfma_scale_f32_16x16x128_f8f6f4 with A = FP4, B = FP8
-// (measured on gfx950): A lane l holds row l%16, K [32(l/16), +32) in 16 bytes
-// (low nibble first); B lane l holds column l%16, K [16(l/16), +16) in bytes
-// 0..15 and K [64 + 16(l/16), +16) in bytes 16..31; the scale operand of lane
-// l applies to K block l/16 of its row/column; the result lane l holds column
-// l%16, rows 4(l/16) .. 4(l/16)+3.
-#include "common.hpp"
-#include "launch.hpp"
+#include "gemm_common.hpp"
 
 namespace moe {
 
 namespace {
-
-template <int OPSEL>
-__device__ __forceinline__ v4f mfma_fp4_fp8(const v4i& a, const v8i& b, const v4f& c, uint32_t sa,
-                                            uint32_t sb) {
-  const v8i a8 = {a.x, a.y, a.z, a.w, 0, 0, 0, 0};
-  // format codes: A = 4 (FP4 E2M1), B = 0 (FP8 E4M3); OPSEL picks the scale byte of this tile
-  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a8, b, c, 4, 0, OPSEL, (int)sa, 0, (int)sb);
-}
 
 // Weight loads: non-temporal (streamed past the caches) when an expert's
 // weights are read once per call, cached when several blocks reuse them.
@@ -72,13 +57,8 @@ __global__ void __launch_bounds__(256) gemm_kernel(GemmArgs args) {
   const int NG = N / (NWR * 64);
   const int nblk = *args.num_padded / bm;
   const int T = nblk * NG;
-  const int wg = blockIdx.x;
-  if (wg >= T) return;
-  // XCD-aware order: workgroup 8j + x runs on XCD x; XCD x takes a contiguous
-  // run of (block, row group) tiles so that the blocks of one expert share L2.
-  const int x = wg & 7, j = wg >> 3;
-  const int q8 = T >> 3, rem = T & 7;
-  const int tile = x * q8 + (x < rem ? x : rem) + j;
+  if ((int)blockIdx.x >= T) return;
+  const int tile = xcd_tile(blockIdx.x, T);
   const int b = tile / NG, wgg = tile - b * NG;
   const int e = args.block_expert[b];
 
@@ -137,8 +117,7 @@ __global__ void __launch_bounds__(256) gemm_kernel(GemmArgs args) {
 #pragma unroll
     for (int c = 0; c < NCG; ++c) {
       if (c < nact) {
-        const v8i bb = {f.b0[c].x, f.b0[c].y, f.b0[c].z, f.b0[c].w,
-                        f.b1[c].x, f.b1[c].y, f.b1[c].z, f.b1[c].w};
+        const v8i bb = join8(f.b0[c], f.b1[c]);
         acc[0][c] = mfma_fp4_fp8<0>(f.a[0], bb, acc[0][c], f.sa, f.sb[c]);
         acc[1][c] = mfma_fp4_fp8<1>(f.a[1], bb, acc[1][c], f.sa, f.sb[c]);
         acc[2][c] = mfma_fp4_fp8<2>(f.a[2], bb, acc[2][c], f.sa, f.sb[c]);
@@ -185,49 +164,14 @@ __global__ void __launch_bounds__(256) gemm_kernel(GemmArgs args) {
           for (int r = 0; r < 4; ++r) acc[t][c][r] += red[p * NWR + wr][t][c][r][lane];
   }
 
-  if constexpr (STAGE == 1) {
-    // lane (t16, g) holds rows 16g + 4t + r of the group: gate/up of the eight
-    // intermediate columns 32*grp + 8g + (2t + r/2); the group's 32 columns are
-    // one quantisation block, spread over the four lanes with equal t16.
-    const int I = N / 2;
 #pragma unroll
-    for (int c = 0; c < NCG; ++c) {
-      if (c < nact) {
-        float h[8];
-#pragma unroll
-        for (int t = 0; t < 4; ++t)
-#pragma unroll
-          for (int q = 0; q < 2; ++q) {
-            const float gate = acc[t][c][2 * q], up = acc[t][c][2 * q + 1];
-            h[2 * t + q] = gate / (1.0f + __expf(-gate)) * up;
-          }
-        float amax = 0.f;
-#pragma unroll
-        for (int q = 0; q < 8; ++q) amax = fmaxf(amax, fabsf(h[q]));
-        amax = fmaxf(amax, __shfl_xor(amax, 16));
-        amax = fmaxf(amax, __shfl_xor(amax, 32));
-        const int E = block_exponent(amax);
-        const uint2 codes = encode8(h, exp2_neg(E));
-        const int64_t p = (int64_t)b * bm + c * 16 + t16;
-        *reinterpret_cast<uint2*>(args.out_q + p * I + grp * 32 + 8 * g) = codes;
-        if (g == 0) args.out_s[p * (I / 32) + grp] = (uint8_t)(E + 127);
-      }
-    }
-  } else {
-    // lane (t16, g) holds output columns 64*grp + 16g + 4t + r of its route:
-    // 16 consecutive floats, so the four lanes of a route write 256 B in a row
-    const int H = N;
-#pragma unroll
-    for (int c = 0; c < NCG; ++c) {
-      if (c < nact && valid[c]) {
-        const int tok = rid[c] & 0xFFFFFF, k = rid[c] >> kSentinelShift;
-        const int64_t slot = (int64_t)tok * args.topk + k;
-        const float wt = args.topk_weights[slot];
-        float4* dst = reinterpret_cast<float4*>(args.y_routes + slot * H + grp * 64 + 16 * g);
-#pragma unroll
-        for (int t = 0; t < 4; ++t)
-          dst[t] = make_float4(wt * acc[t][c][0], wt * acc[t][c][1], wt * acc[t][c][2], wt * acc[t][c][3]);
-      }
+  for (int c = 0; c < NCG; ++c) {
+    if (c < nact) {
+      const v4f part[4] = {acc[0][c], acc[1][c], acc[2][c], acc[3][c]};
+      if constexpr (STAGE == 1)
+        stage1_store(part, (int64_t)b * bm + c * 16 + t16, grp, N / 2, g, args.out_q, args.out_s);
+      else if (valid[c])
+        stage2_store(part, rid[c], args, grp, g);
     }
   }
 }
@@ -254,24 +198,30 @@ hipError_t launch_gemm(const GemmArgs& a, int64_t max_blocks, hipStream_t stream
 #ifndef MOE_NT_SMALL
 #define MOE_NT_SMALL true
 #endif
+// smallest block size that goes to the LDS-tiled kernel of gemm_tile.hip
+#ifndef MOE_TILE_MIN_BM
+#define MOE_TILE_MIN_BM 64
+#endif
 
 }  // namespace
 
 hipError_t launch_stage1(const GemmArgs& a, int64_t max_blocks, hipStream_t stream) {
+  if (a.bm >= MOE_TILE_MIN_BM) return launch_tile(1, a, max_blocks, stream);
   switch (a.bm) {
     case 16: return launch_gemm<1, 1, MOE_S1_NWK_SMALL, MOE_S1_PD, MOE_NT_SMALL>(a, max_blocks, stream);
     case 32: return launch_gemm<1, 2, MOE_S1_NWK_SMALL, MOE_S1_PD, MOE_NT_SMALL>(a, max_blocks, stream);
-    case 64: return launch_gemm<1, 4, 1, 2, false>(a, max_blocks, stream);
+    case 64: return launch_gemm<1, 4, MOE_S1_NWK_SMALL, MOE_S1_PD, MOE_NT_SMALL>(a, max_blocks, stream);
     case 128: return launch_gemm<1, 8, 1, 2, false>(a, max_blocks, stream);
     default: return hipErrorInvalidValue;
   }
 }
 
 hipError_t launch_stage2(const GemmArgs& a, int64_t max_blocks, hipStream_t stream) {
+  if (a.bm >= MOE_TILE_MIN_BM) return launch_tile(2, a, max_blocks, stream);
   switch (a.bm) {
     case 16: return launch_gemm<2, 1, 1, MOE_S2_PD, MOE_NT_SMALL>(a, max_blocks, stream);
     case 32: return launch_gemm<2, 2, 1, MOE_S2_PD, MOE_NT_SMALL>(a, max_blocks, stream);
-    case 64: return launch_gemm<2, 4, 1, 2, false>(a, max_blocks, stream);
+    case 64: return launch_gemm<2, 4, 1, MOE_S2_PD, MOE_NT_SMALL>(a, max_blocks, stream);
     case 128: return launch_gemm<2, 8, 1, 2, false>(a, max_blocks, stream);
     default: return hipErrorInvalidValue;
   }

@@ -1,0 +1,79 @@
+// Pieces shared by the two grouped-GEMM kernels of the A8W4 MoE layer
+// (gemm.hip for decode-sized blocks, gemm_tile.hip for larger ones): the
+// scaled MFMA, the XCD-aware tile order and the two epilogues.
+#pragma once
+
+#include "common.hpp"
+#include "launch.hpp"
+
+namespace moe {
+
+// v_mfma_scale_f32_16x16x128_f8f6f4 with A = FP4 weights (format 4) and B = FP8
+// tokens (format 0).  Operand layout (measured on gfx950): A lane l holds row
+// l%16, K [32(l/16), +32) in 16 bytes, low nibble first; B lane l holds column
+// l%16, K [16(l/16), +16) in bytes 0..15 and K [64 + 16(l/16), +16) in bytes
+// 16..31; the scale operand of lane l applies to K block l/16; the result lane
+// l holds column l%16, rows 4(l/16) .. 4(l/16)+3.  OPSEL picks the scale byte.
+template <int OPSEL>
+__device__ __forceinline__ v4f mfma_fp4_fp8(const v4i& a, const v8i& b, const v4f& c, uint32_t sa,
+                                            uint32_t sb) {
+  const v8i a8 = {a.x, a.y, a.z, a.w, 0, 0, 0, 0};
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a8, b, c, 4, 0, OPSEL, (int)sa, 0, (int)sb);
+}
+
+__device__ __forceinline__ v8i join8(const v4i& lo, const v4i& hi) {
+  return v8i{lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+}
+
+// Workgroup 8j + x runs on XCD x; XCD x takes a contiguous run of the T tiles
+// so that neighbouring tiles (the blocks of one expert) share that XCD's L2.
+__device__ __forceinline__ int xcd_tile(int wg, int T) {
+  const int x = wg & 7, j = wg >> 3;
+  const int q8 = T >> 3, rem = T & 7;
+  return x * q8 + (x < rem ? x : rem) + j;
+}
+
+// Stage-one epilogue for one 64-row group and one 16-token column group of a
+// wave: lane (t16, g) holds, in acc[t], rows 16g + 4t + r of the group, i.e.
+// gate (r even) and up (r odd) of intermediate columns 32 grp + 8g + 2t + r/2.
+// h = SiLU(gate) * up; the group's 32 columns form one per-1x32 quantisation
+// block, spread over the four lanes with equal t16.  Writes row p of the
+// intermediate (8 codes per lane, the scale from lane g = 0).  All 64 lanes
+// must call it together.
+__device__ __forceinline__ void stage1_store(const v4f acc[4], int64_t p, int grp, int I, int g,
+                                             uint8_t* __restrict__ out_q, uint8_t* __restrict__ out_s) {
+  float h[8];
+#pragma unroll
+  for (int t = 0; t < 4; ++t)
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+      const float gate = acc[t][2 * q], up = acc[t][2 * q + 1];
+      h[2 * t + q] = gate / (1.0f + __expf(-gate)) * up;
+    }
+  float amax = 0.f;
+#pragma unroll
+  for (int q = 0; q < 8; ++q) amax = fmaxf(amax, fabsf(h[q]));
+  amax = fmaxf(amax, __shfl_xor(amax, 16));
+  amax = fmaxf(amax, __shfl_xor(amax, 32));
+  const int E = block_exponent(amax);
+  *reinterpret_cast<uint2*>(out_q + p * I + grp * 32 + 8 * g) = encode8(h, exp2_neg(E));
+  if (g == 0) out_s[p * (I / 32) + grp] = (uint8_t)(E + 127);
+}
+
+// Stage-two epilogue: lane (t16, g) holds output columns 64 grp + 16g + 4t + r
+// of one route; writes topk_weight * value to that route's row, 16 consecutive
+// floats per lane (the four lanes of a route write 256 B in a row).  The rows
+// stay in float32: routes of one token can cancel, and a BF16 rounding of
+// each route's share would then exceed the output tolerance.
+__device__ __forceinline__ void stage2_store(const v4f acc[4], int rid, const GemmArgs& args,
+                                             int grp, int g) {
+  const int tok = rid & 0xFFFFFF, k = rid >> kSentinelShift;
+  const int64_t slot = (int64_t)tok * args.topk + k;
+  const float wt = args.topk_weights[slot];
+  float4* dst = reinterpret_cast<float4*>(args.y_routes + slot * args.N + grp * 64 + 16 * g);
+#pragma unroll
+  for (int t = 0; t < 4; ++t)
+    dst[t] = make_float4(wt * acc[t][0], wt * acc[t][1], wt * acc[t][2], wt * acc[t][3]);
+}
+
+}  // namespace moe

@@ -1,0 +1,290 @@
+// Grouped GEMMs of the A8W4 MoE layer for blocks of 64 or 128 routes, where an
+// expert's rows are many enough that the MFMAs, not the weight stream, bound
+// the time.  Same computation and epilogues as gemm.hip (stage one: SiLU(gate)
+// * up and per-1x32 FP8 requantisation of the intermediate; stage two: routing
+// weight and per-route rows; aiter PR 5609, "Add DeepSeek V4.1 Flash TP4
+// gfx950 MoE tuning", Configuration), organised for operand reuse:
+//
+//   workgroup tile  256 weight rows x BM tokens (BM = 32 CGW), 4 waves as
+//                   2 x 2: wave (wr, wc) computes rows [128 wr, +128) (two
+//                   64-row groups, 8 MFMA tiles) x tokens [wc BM/2, +BM/2)
+//   K step          128: 16 KB of packed weights, BM x 128 B of token codes,
+//                   1 KB of weight scales and BM x 4 B of token scales
+//   staging         a ring of S such steps in LDS, filled by direct
+//                   global-to-LDS loads (no registers involved), S - 1 steps
+//                   in flight while the MFMAs consume one; one barrier per
+//                   step.
+//
+// LDS layout of one step (offsets in bytes):
+//   A   [4 row groups][4 tiles][64 lanes][16]   the packed chunk as stored
+//   B   [BM tokens][8 slots of 16]              piece p of token t sits in slot
+//                                               p ^ ((t >> 1) & 7), so the 16
+//                                               lanes of one operand read hit 16
+//                                               distinct 16-byte bank slots
+//   As  [4 row groups][64 lanes][4]             E8M0 weight scales
+//   Bs  [4 copies][64 tokens][4]                E8M0 token scales; wave w loads
+//                                               tokens 64 (w mod BM/64) + lane,
+//                                               so tokens 0..BM-1 sit in order
+//                                               at the start of the area
+//
+// Each wave issues the same number of loads per step, so one vmcnt value
+// tells every wave that its share of a step has landed; the barrier then
+// publishes all shares and frees the slot that was read one step earlier.
+#include "gemm_common.hpp"
+
+namespace moe {
+
+namespace {
+
+typedef __attribute__((address_space(3))) void* lds_ptr;
+
+// M0 carries the LDS base of the direct loads below; no other code of this
+// kernel uses M0 (clang warns about naming a reserved register as clobbered).
+#pragma clang diagnostic ignored "-Winline-asm"
+
+// Direct global-to-LDS loads: lane l's 16 (or 4) bytes at g go to LDS byte
+// lds + 16 l (or 4 l); lds must be the same in every lane.  Written as inline
+// assembly so that the compiler, which cannot tell the ring's slots apart,
+// does not wait for every load in flight before each LDS read; the kernel
+// waits for them itself (vmcnt) before the barrier that publishes a slot.
+__device__ __forceinline__ void dma16(const void* g, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(g), "s"(lds)
+               : "memory", "m0");
+}
+__device__ __forceinline__ void dma4(const void* g, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dword %0, off" ::"v"(g), "s"(lds)
+               : "memory", "m0");
+}
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(lds_ptr)p);
+}
+
+template <int CGW>
+struct TileGeom {
+  static constexpr int BM = 32 * CGW;
+  static constexpr int A = 0;
+  static constexpr int B = 16384;
+  static constexpr int AS = B + BM * 128;
+  static constexpr int BS = AS + 1024;
+  static constexpr int BYTES = BS + 1024;
+  static constexpr int LOADS = 4 + CGW + 2;   // per wave and step: A, B chunks, As, Bs
+};
+
+// s_waitcnt immediates (gfx9 encoding): wait on the vector-memory counter
+// only, or on the LDS/scalar counter only.
+constexpr int vmcnt_only(int n) { return (n & 15) | (((n >> 4) & 3) << 14) | (7 << 4) | (15 << 8); }
+constexpr int lgkmcnt_zero() { return 15 | (3 << 14) | (7 << 4); }
+
+// A workgroup barrier without the memory fences of __syncthreads (those would
+// also wait for every direct-to-LDS load still in flight).
+__device__ __forceinline__ void barrier_only() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+// Tile order.  In block-major order (t = b NT + wgt) the tiles of one expert
+// form the run [f NT, (f + nb) NT), f its first block and nb its block count.
+// Inside that run the tiles are taken slice-major (wgt = l / nb, b = f + l % nb)
+// so that the nb blocks that read the same 256-row weight slice run side by
+// side on one XCD and share it through its L2, while the expert's token
+// blocks stay resident there across the slices.  f and nb come from the run
+// of equal entries of block_expert around block t / NT (every wave finds
+// them itself with two 64-wide ballots; block_expert is sorted).
+__device__ __forceinline__ void expert_major(int t, int NT, int nblk, const int32_t* __restrict__ block_expert,
+                                             int& b, int& wgt) {
+  const int lane = threadIdx.x & 63;
+  const int b0 = t / NT;
+  const int e = block_expert[b0];
+  int back = 0;   // blocks of e at or before b0
+  for (;;) {
+    const int idx = b0 - back - lane;
+    const bool eq = idx >= 0 && block_expert[idx] == e;
+    const unsigned long long m = __ballot(eq);
+    const int run = (~m == 0ull) ? 64 : __builtin_ctzll(~m);
+    back += run;
+    if (run < 64) break;
+  }
+  int fwd = 0;    // blocks of e after b0
+  for (;;) {
+    const int idx = b0 + 1 + fwd + lane;
+    const bool eq = idx < nblk && block_expert[idx] == e;
+    const unsigned long long m = __ballot(eq);
+    const int run = (~m == 0ull) ? 64 : __builtin_ctzll(~m);
+    fwd += run;
+    if (run < 64) break;
+  }
+  const int f = b0 - back + 1, nb = back + fwd;
+  const int l = t - f * NT;
+  wgt = l / nb;
+  b = f + (l - wgt * nb);
+}
+
+template <int STAGE, int CGW, int S, int WPE>
+__global__ void __launch_bounds__(256, WPE) tile_kernel(GemmArgs args) {
+  using G = TileGeom<CGW>;
+  constexpr int BM = G::BM;
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[S][G::BYTES];
+
+  const int N = args.N, K = args.K, M = args.M;
+  const int KS = K / 128;
+  const int NT = N / 256;
+  const int nblk = *args.num_padded / BM;
+  const int T = nblk * NT;
+  if ((int)blockIdx.x >= T) return;
+  int b, wgt;
+  expert_major(xcd_tile(blockIdx.x, T), NT, nblk, args.block_expert, b, wgt);
+  const int e = args.block_expert[b];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform: LDS bases go to M0
+  const int wr = wave >> 1, wc = wave & 1;
+  const int t16 = lane & 15, g = lane >> 4;
+  const int32_t* ids = args.sorted_ids + (int64_t)b * BM;
+  const int first = ids[0];   // a block always starts with a route
+
+  // B row of block token t; padding tokens read a real row (their columns
+  // are never stored, the load only has to stay in bounds)
+  auto brow = [&](int t) -> int64_t {
+    if (STAGE == 1) {
+      const int r = ids[t];
+      return (int64_t)((r == M ? first : r) & 0xFFFFFF);
+    }
+    return (int64_t)b * BM + t;
+  };
+
+  // per-lane global sources of this wave's loads, at step 0
+  const uint8_t* gA = args.w + (int64_t)e * ((int64_t)N * K / 2) +
+                      (int64_t)(wgt * 4 + wave) * KS * 4096 + lane * 16;
+  const uint8_t* gAs = args.ws + (int64_t)e * ((int64_t)N * K / 32) +
+                       (int64_t)(wgt * 4 + wave) * KS * 256 + lane * 4;
+  const uint8_t* gB[CGW];
+#pragma unroll
+  for (int i = 0; i < CGW; ++i) {
+    const int t = 8 * (wave * CGW + i) + (lane >> 3);
+    const int piece = (lane & 7) ^ ((t >> 1) & 7);
+    gB[i] = args.bq + brow(t) * K + piece * 16;
+  }
+  constexpr int NBS = BM / 64;
+  const uint8_t* gBs = args.bs + brow((wave % NBS) * 64 + lane) * (K / 32);
+
+  const uint32_t lds0 = lds_addr(&smem[0][0]);
+  auto issue = [&](int s) {
+    const uint32_t base = lds0 + (uint32_t)(s % S) * G::BYTES;
+#pragma unroll
+    for (int t = 0; t < 4; ++t) dma16(gA + (int64_t)s * 4096 + t * 1024, base + G::A + wave * 4096 + t * 1024);
+#pragma unroll
+    for (int i = 0; i < CGW; ++i) dma16(gB[i] + s * 128, base + G::B + (wave * CGW + i) * 1024);
+    dma4(gAs + (int64_t)s * 256, base + G::AS + wave * 256);
+    dma4(gBs + 4 * s, base + G::BS + wave * 256);
+  };
+
+  // the K loop and epilogue for NA active 16-token column groups of this
+  // wave (columns past the block's last route are skipped); every wave takes
+  // its share of the loads and every barrier whatever its NA
+  auto run = [&](auto na_tag) {
+    constexpr int NA = decltype(na_tag)::value;
+    v4f acc[2][4][NA > 0 ? NA : 1];
+#pragma unroll
+    for (int rg = 0; rg < 2; ++rg)
+#pragma unroll
+      for (int t = 0; t < 4; ++t)
+#pragma unroll
+        for (int c = 0; c < NA; ++c) acc[rg][t][c] = v4f{0.f, 0.f, 0.f, 0.f};
+
+#pragma unroll
+    for (int s = 0; s < S - 1; ++s)
+      if (s < KS) issue(s);
+    for (int s = 0; s < KS; ++s) {
+      // this wave's loads of step s have landed once at most the loads of
+      // the steps after it are outstanding
+      if (s + S - 2 < KS) __builtin_amdgcn_s_waitcnt(vmcnt_only((S - 2) * G::LOADS));
+      else __builtin_amdgcn_s_waitcnt(vmcnt_only(0));
+      __builtin_amdgcn_s_waitcnt(lgkmcnt_zero());   // this wave's reads of step s - 1 are done
+      barrier_only();
+      if (s + S - 1 < KS) issue(s + S - 1);
+      if constexpr (NA > 0) {
+        const uint8_t* base = smem[s % S];
+        v4i a[2][4];
+        uint32_t sa[2];
+#pragma unroll
+        for (int rg = 0; rg < 2; ++rg) {
+#pragma unroll
+          for (int t = 0; t < 4; ++t)
+            a[rg][t] = *reinterpret_cast<const v4i*>(base + G::A + (2 * wr + rg) * 4096 + t * 1024 + lane * 16);
+          sa[rg] = *reinterpret_cast<const uint32_t*>(base + G::AS + (2 * wr + rg) * 256 + lane * 4);
+        }
+#pragma unroll
+        for (int c = 0; c < NA; ++c) {
+          const int tok = wc * CGW * 16 + c * 16 + t16;
+          const int sw = (tok >> 1) & 7;
+          const uint8_t* row = base + G::B + tok * 128;
+          const v8i bb = join8(*reinterpret_cast<const v4i*>(row + ((g ^ sw) << 4)),
+                               *reinterpret_cast<const v4i*>(row + (((4 + g) ^ sw) << 4)));
+          const uint32_t sb = (*reinterpret_cast<const uint32_t*>(base + G::BS + tok * 4) >> (8 * g)) & 0xFFu;
+#pragma unroll
+          for (int rg = 0; rg < 2; ++rg) {
+            acc[rg][0][c] = mfma_fp4_fp8<0>(a[rg][0], bb, acc[rg][0][c], sa[rg], sb);
+            acc[rg][1][c] = mfma_fp4_fp8<1>(a[rg][1], bb, acc[rg][1][c], sa[rg], sb);
+            acc[rg][2][c] = mfma_fp4_fp8<2>(a[rg][2], bb, acc[rg][2][c], sa[rg], sb);
+            acc[rg][3][c] = mfma_fp4_fp8<3>(a[rg][3], bb, acc[rg][3][c], sa[rg], sb);
+          }
+        }
+      }
+    }
+
+#pragma unroll
+    for (int rg = 0; rg < 2; ++rg) {
+      const int grp = wgt * 4 + 2 * wr + rg;
+#pragma unroll
+      for (int c = 0; c < NA; ++c) {
+        const v4f part[4] = {acc[rg][0][c], acc[rg][1][c], acc[rg][2][c], acc[rg][3][c]};
+        const int col = wc * CGW * 16 + c * 16 + t16;
+        if constexpr (STAGE == 1) {
+          stage1_store(part, (int64_t)b * BM + col, grp, N / 2, g, args.out_q, args.out_s);
+        } else {
+          const int rid = ids[col];
+          if (rid != M) stage2_store(part, rid, args, grp, g);
+        }
+      }
+    }
+  };
+
+  int nact = 0;
+#pragma unroll
+  for (int c = 0; c < CGW; ++c)
+    if (__ballot(ids[wc * CGW * 16 + c * 16 + t16] != M) != 0) nact = c + 1;
+  nact = __builtin_amdgcn_readfirstlane(nact);
+  if (nact == CGW) run(std::integral_constant<int, CGW>{});
+  else if (nact == 0) run(std::integral_constant<int, 0>{});
+  else if (nact == 1) run(std::integral_constant<int, 1>{});
+  else if constexpr (CGW > 2) {
+    if (nact == 2) run(std::integral_constant<int, 2>{});
+    else run(std::integral_constant<int, 3>{});
+  }
+}
+
+// ring depth and waves per SIMD: 2 steps and 2 workgroups per CU (69.6 KB of
+// LDS each at BM = 128), or 3 steps and one
+#ifndef MOE_TILE_STAGES
+#define MOE_TILE_STAGES 2
+#endif
+#ifndef MOE_TILE_WPE
+#define MOE_TILE_WPE 2
+#endif
+
+}  // namespace
+
+hipError_t launch_tile(int stage, const GemmArgs& a, int64_t max_blocks, hipStream_t stream) {
+  constexpr int S = MOE_TILE_STAGES, W = MOE_TILE_WPE;
+  const int64_t grid = max_blocks * (a.N / 256);
+  if (grid <= 0) return hipSuccess;
+  const dim3 g((unsigned)grid), blk(256);
+  if (stage == 1 && a.bm == 128) hipLaunchKernelGGL((tile_kernel<1, 4, S, W>), g, blk, 0, stream, a);
+  else if (stage == 1 && a.bm == 64) hipLaunchKernelGGL((tile_kernel<1, 2, S, W>), g, blk, 0, stream, a);
+  else if (stage == 2 && a.bm == 128) hipLaunchKernelGGL((tile_kernel<2, 4, S, W>), g, blk, 0, stream, a);
+  else if (stage == 2 && a.bm == 64) hipLaunchKernelGGL((tile_kernel<2, 2, S, W>), g, blk, 0, stream, a);
+  else return hipErrorInvalidValue;
+  return hipGetLastError();
+}
+
+}  // namespace moe

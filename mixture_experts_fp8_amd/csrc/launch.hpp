@@ -38,5 +38,7 @@ hipError_t launch_pack(const uint8_t* src, const uint8_t* src_s, uint8_t* dst, u
 // max_blocks: upper bound of sorted blocks (grid size); kernels read the real count on device
 hipError_t launch_stage1(const GemmArgs& a, int64_t max_blocks, hipStream_t stream);
 hipError_t launch_stage2(const GemmArgs& a, int64_t max_blocks, hipStream_t stream);
+// LDS-tiled variant of either stage for bm = 64 or 128 (gemm_tile.hip)
+hipError_t launch_tile(int stage, const GemmArgs& a, int64_t max_blocks, hipStream_t stream);
 
 }  // namespace moe

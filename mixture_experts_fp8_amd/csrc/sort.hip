@@ -16,15 +16,22 @@
 // Routes whose expert lies outside [expert_offset, expert_offset + E) are
 // dropped.
 //
-// One workgroup of 16 waves.  Wave w owns the contiguous routes
-// [w C, (w+1) C), C = ceil(R / 16):
-//   1. each wave counts its routes per expert (LDS atomics; counts only);
+// The routes are cut into NS contiguous chunks, one workgroup of 16 waves
+// per chunk (NS = 1 up to 4096 routes).  Every workgroup counts all routes per
+// expert (so each knows every expert's padded start and how many of the
+// expert's routes lie in earlier chunks; no data passes between workgroups),
+// then places its own chunk.  Wave w of a workgroup owns the contiguous
+// routes [w C, (w+1) C) of the chunk, C = ceil(chunk / 16):
+//   1. count: per expert in total, before this chunk, and per wave of it
+//      (LDS atomics; counts only);
 //   2. one scan gives every expert its padded start and every (wave, expert)
-//      the offset of that wave's first route of the expert;
-//   3. each wave walks its chunk 64 routes at a time; the rank of a route
-//      among same-expert routes of the piece is a popcount of a wave-private
-//      64-bit lane mask (ds_or_b64), so no barrier or atomic ordering is
-//      involved and the result is deterministic.
+//      the position of that wave's first route of the expert;
+//   3. each wave walks its routes 64 at a time; the lanes holding the same
+//      expert are found with one ballot per bit of the expert id, and the
+//      rank of a route among them is a popcount of that lane mask, so no
+//      barrier or atomic ordering is involved and the result is
+//      deterministic.
+// Workgroup 0 also writes the padding, the block experts and num_padded.
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -35,11 +42,20 @@ namespace {
 constexpr int kPrepThreads = 1024;
 constexpr int kSortWaves = kPrepThreads / kWave;
 
+constexpr int kRoutesPerSortBlock = 4096;
+constexpr int kMaxSortBlocks = 64;
+
 struct SortSmem {
   int cnt[kSortWaves][kMaxExperts];                 // per-wave counts, then running offsets
-  unsigned long long mask[kSortWaves][kMaxExperts]; // per-wave lane masks of one 64-route piece
+  int total[kMaxExperts];                           // routes per expert
+  int before[kMaxExperts];                          // of which in earlier chunks
   int wave_total[kSortWaves];
 };
+
+int sort_blocks(int64_t R) {
+  const int64_t n = (R + kRoutesPerSortBlock - 1) / kRoutesPerSortBlock;
+  return (int)(n < 1 ? 1 : (n > kMaxSortBlocks ? kMaxSortBlocks : n));
+}
 
 // Orders this wave's LDS accesses before and after (all lanes of a wave run
 // in lockstep; the fences keep the compiler from reordering across this point
@@ -50,32 +66,47 @@ __device__ __forceinline__ void wave_sync() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
-__device__ void sort_block(SortSmem& sm, const int32_t* __restrict__ ids, int M, int topk, int E,
-                           int expert_offset, int bm, int32_t* __restrict__ sorted_ids,
-                           int32_t* __restrict__ block_expert, int32_t* __restrict__ num_padded) {
+__device__ void sort_chunk(SortSmem& sm, const int32_t* __restrict__ ids, int M, int topk, int E,
+                           int expert_offset, int bm, int chunk, int nchunks,
+                           int32_t* __restrict__ sorted_ids, int32_t* __restrict__ block_expert,
+                           int32_t* __restrict__ num_padded) {
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int R = M * topk;
-  const int C = (R + kSortWaves - 1) / kSortWaves;
-  const int f0 = w * C, f1 = min(R, f0 + C);
+  const int CH = (R + nchunks - 1) / nchunks;
+  const int g0 = min(R, chunk * CH), g1 = min(R, g0 + CH);
+  const int C = (g1 - g0 + kSortWaves - 1) / kSortWaves;
+  const int f0 = g0 + w * C, f1 = min(g1, f0 + C);
 
-  for (int i = tid; i < kSortWaves * kMaxExperts; i += kPrepThreads) {
-    (&sm.cnt[0][0])[i] = 0;
-    (&sm.mask[0][0])[i] = 0ull;
+  for (int i = tid; i < kSortWaves * kMaxExperts; i += kPrepThreads) (&sm.cnt[0][0])[i] = 0;
+  for (int i = tid; i < kMaxExperts; i += kPrepThreads) {
+    sm.total[i] = 0;
+    sm.before[i] = 0;
   }
   __syncthreads();
 
-  // 1. per-wave histogram of local routes
-  for (int f = f0 + lane; f < f1; f += 64) {
-    const int le = ids[f] - expert_offset;
-    if ((unsigned)le < (unsigned)E) atomicAdd(&sm.cnt[w][le], 1);
+  // 1. counts over all routes: total, before this chunk, per owning wave
+  constexpr int U = 4;
+  for (int base = 0; base < R; base += U * kPrepThreads) {
+    int le[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int f = base + u * kPrepThreads + tid;
+      le[u] = f < R ? ids[f] - expert_offset : -1;
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int f = base + u * kPrepThreads + tid;
+      if ((unsigned)le[u] < (unsigned)E) {
+        atomicAdd(&sm.total[le[u]], 1);
+        if (f < g0) atomicAdd(&sm.before[le[u]], 1);
+        else if (f < g1) atomicAdd(&sm.cnt[(f - g0) / C][le[u]], 1);
+      }
+    }
   }
   __syncthreads();
 
   // 2. one expert per thread: its count, padded size, and the waves' offsets
-  int c = 0;
-  if (tid < E) {
-    for (int j = 0; j < kSortWaves; ++j) c += sm.cnt[j][tid];
-  }
+  const int c = tid < E ? sm.total[tid] : 0;
   const int pc = (c + bm - 1) / bm * bm;
   int v = pc;
 #pragma unroll
@@ -93,20 +124,23 @@ __device__ void sort_block(SortSmem& sm, const int32_t* __restrict__ ids, int M,
   }
   const int start = before + v - pc;
   if (tid < E) {
-    int run = start;
+    int run = start + sm.before[tid];
     for (int j = 0; j < kSortWaves; ++j) {  // counts become each wave's first position
       const int n = sm.cnt[j][tid];
       sm.cnt[j][tid] = run;
       run += n;
     }
-    for (int p = start + c; p < start + pc; ++p) sorted_ids[p] = M;
-    for (int b = start / bm; b < (start + pc) / bm; ++b) block_expert[b] = tid;
+    if (chunk == 0) {
+      for (int p = start + c; p < start + pc; ++p) sorted_ids[p] = M;
+      for (int b = start / bm; b < (start + pc) / bm; ++b) block_expert[b] = tid;
+    }
   }
-  if (tid == 0) *num_padded = total;
+  if (chunk == 0 && tid == 0) *num_padded = total;
   __syncthreads();
 
   // 3. each wave places its own routes in order; only wave-private LDS is used
-  const unsigned long long bit = 1ull << lane;
+  static_assert(kMaxExperts <= 1023, "expert key needs more bits");
+  const unsigned long long below = (1ull << lane) - 1;
   for (int base = f0; base < f1; base += 64) {
     const int f = base + lane;
     int le = -1;
@@ -114,21 +148,21 @@ __device__ void sort_block(SortSmem& sm, const int32_t* __restrict__ ids, int M,
       le = ids[f] - expert_offset;
       if ((unsigned)le >= (unsigned)E) le = -1;
     }
-    if (le >= 0) atomicOr(&sm.mask[w][le], bit);
-    wave_sync();
-    unsigned long long m = 0;
-    int rank = 0;
+    const int key = le + 1;   // 0 for no local route
+    unsigned long long same = ~0ull;
+#pragma unroll
+    for (int bit = 0; bit < 10; ++bit) {
+      const bool on = (key >> bit) & 1;
+      const unsigned long long m = __ballot(on);
+      same &= on ? m : ~m;
+    }
+    const int rank = __popcll(same & below);
     if (le >= 0) {
-      m = sm.mask[w][le];
-      rank = __popcll(m & (bit - 1));
       const int t = f / topk, k = f - t * topk;
       sorted_ids[sm.cnt[w][le] + rank] = (k << kSentinelShift) | t;
     }
     wave_sync();
-    if (le >= 0 && rank == 0) {
-      sm.cnt[w][le] += __popcll(m);
-      sm.mask[w][le] = 0ull;
-    }
+    if (le >= 0 && rank == 0) sm.cnt[w][le] += __popcll(same);
     wave_sync();
   }
 }
@@ -136,46 +170,60 @@ __device__ void sort_block(SortSmem& sm, const int32_t* __restrict__ ids, int M,
 // Four lanes own one 32-element block: lane i of the quad loads 8 BF16 values
 // (16 B), so a wave reads 1 KB contiguous per load and writes 512 B of codes.
 // FP8 activations with one E8M0 scale per 1x32 block (aiter PR 5609,
-// Configuration).  n8 and the stride are multiples of 4, so a quad is either
-// all in range or all out.
-__device__ void quant_range(const uint16_t* __restrict__ x, uint8_t* __restrict__ q,
-                            uint8_t* __restrict__ s, int64_t n8, int64_t first, int64_t stride) {
-  for (int64_t i = first; i < n8; i += stride) {
-    const uint4 raw = *reinterpret_cast<const uint4*>(x + i * 8);
-    float v[8];
-    v[0] = bf16_to_f32(raw.x & 0xFFFFu); v[1] = bf16_to_f32(raw.x >> 16);
-    v[2] = bf16_to_f32(raw.y & 0xFFFFu); v[3] = bf16_to_f32(raw.y >> 16);
-    v[4] = bf16_to_f32(raw.z & 0xFFFFu); v[5] = bf16_to_f32(raw.z >> 16);
-    v[6] = bf16_to_f32(raw.w & 0xFFFFu); v[7] = bf16_to_f32(raw.w >> 16);
-    float amax = 0.0f;
+// Configuration).  Each thread has U loads in flight.  n8 and the stride are
+// multiples of 4, so a quad is either all in range or all out.
+__device__ __forceinline__ void quant_one(uint4 raw, int64_t i, uint8_t* __restrict__ q,
+                                          uint8_t* __restrict__ s) {
+  float v[8];
+  v[0] = bf16_to_f32(raw.x & 0xFFFFu); v[1] = bf16_to_f32(raw.x >> 16);
+  v[2] = bf16_to_f32(raw.y & 0xFFFFu); v[3] = bf16_to_f32(raw.y >> 16);
+  v[4] = bf16_to_f32(raw.z & 0xFFFFu); v[5] = bf16_to_f32(raw.z >> 16);
+  v[6] = bf16_to_f32(raw.w & 0xFFFFu); v[7] = bf16_to_f32(raw.w >> 16);
+  float amax = 0.0f;
 #pragma unroll
-    for (int j = 0; j < 8; ++j) amax = fmaxf(amax, fabsf(v[j]));
-    amax = fmaxf(amax, __shfl_xor(amax, 1));
-    amax = fmaxf(amax, __shfl_xor(amax, 2));
-    const int E = block_exponent(amax);
-    *reinterpret_cast<uint2*>(q + i * 8) = encode8(v, exp2_neg(E));
-    if ((i & 3) == 0) s[i >> 2] = (uint8_t)(E + 127);
-  }
+  for (int j = 0; j < 8; ++j) amax = fmaxf(amax, fabsf(v[j]));
+  amax = fmaxf(amax, __shfl_xor(amax, 1));
+  amax = fmaxf(amax, __shfl_xor(amax, 2));
+  const int E = block_exponent(amax);
+  *reinterpret_cast<uint2*>(q + i * 8) = encode8(v, exp2_neg(E));
+  if ((i & 3) == 0) s[i >> 2] = (uint8_t)(E + 127);
 }
 
-// Workgroup 0 sorts (if ids != nullptr); workgroups 1.. quantise (if x != nullptr).
-__global__ void __launch_bounds__(kPrepThreads) prep_kernel(
-    const int32_t* __restrict__ ids, int M, int topk, int E, int expert_offset, int bm,
-    int32_t* __restrict__ sorted_ids, int32_t* __restrict__ block_expert,
-    int32_t* __restrict__ num_padded, const uint16_t* __restrict__ x, uint8_t* __restrict__ q,
-    uint8_t* __restrict__ s, int64_t n8) {
-  __shared__ SortSmem sm;
-  if (blockIdx.x == 0) {
-    if (ids) sort_block(sm, ids, M, topk, E, expert_offset, bm, sorted_ids, block_expert, num_padded);
-    return;
+__device__ void quant_range(const uint16_t* __restrict__ x, uint8_t* __restrict__ q,
+                            uint8_t* __restrict__ s, int64_t n8, int64_t first, int64_t stride) {
+  constexpr int U = 4;
+  int64_t i = first;
+  for (; i + (U - 1) * stride < n8; i += U * stride) {
+    v4i raw[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+      raw[u] = __builtin_nontemporal_load(reinterpret_cast<const v4i*>(x + (i + u * stride) * 8));
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+      quant_one(make_uint4(raw[u].x, raw[u].y, raw[u].z, raw[u].w), i + u * stride, q, s);
   }
-  quant_range(x, q, s, n8, (int64_t)(blockIdx.x - 1) * kPrepThreads + threadIdx.x,
-              (int64_t)(gridDim.x - 1) * kPrepThreads);
+  for (; i < n8; i += stride) quant_one(*reinterpret_cast<const uint4*>(x + i * 8), i, q, s);
 }
 
 int quant_blocks(int64_t n8) {
   int64_t b = (n8 + kPrepThreads - 1) / kPrepThreads;
   return (int)(b > 1024 ? 1024 : b);
+}
+
+// Workgroups 0 .. ns-1 sort (ns = 0 without ids); the others quantise.
+__global__ void __launch_bounds__(kPrepThreads) prep_kernel(
+    const int32_t* __restrict__ ids, int M, int topk, int E, int expert_offset, int bm, int ns,
+    int32_t* __restrict__ sorted_ids, int32_t* __restrict__ block_expert,
+    int32_t* __restrict__ num_padded, const uint16_t* __restrict__ x, uint8_t* __restrict__ q,
+    uint8_t* __restrict__ s, int64_t n8) {
+  __shared__ SortSmem sm;
+  if ((int)blockIdx.x < ns) {
+    sort_chunk(sm, ids, M, topk, E, expert_offset, bm, blockIdx.x, ns, sorted_ids, block_expert,
+               num_padded);
+    return;
+  }
+  quant_range(x, q, s, n8, (int64_t)(blockIdx.x - ns) * kPrepThreads + threadIdx.x,
+              (int64_t)(gridDim.x - ns) * kPrepThreads);
 }
 
 }  // namespace
@@ -184,10 +232,11 @@ hipError_t launch_prep(const int32_t* ids, int32_t M, int32_t topk, int32_t E, i
                        int32_t bm, int32_t* sorted_ids, int32_t* block_expert, int32_t* num_padded,
                        const uint16_t* x, int64_t H, uint8_t* q, uint8_t* s, hipStream_t stream) {
   const int64_t n8 = x ? (int64_t)M * H / 8 : 0;
-  const int grid = 1 + (n8 > 0 ? quant_blocks(n8) : 0);
-  if (!ids && grid == 1) return hipSuccess;
+  const int ns = ids ? sort_blocks((int64_t)M * topk) : 0;
+  const int grid = ns + (n8 > 0 ? quant_blocks(n8) : 0);
+  if (grid == 0) return hipSuccess;
   hipLaunchKernelGGL(prep_kernel, dim3(grid), dim3(kPrepThreads), 0, stream, ids, M, topk, E,
-                     expert_offset, bm, sorted_ids, block_expert, num_padded, x, q, s, n8);
+                     expert_offset, bm, ns, sorted_ids, block_expert, num_padded, x, q, s, n8);
   return hipGetLastError();
 }
 

@@ -34,7 +34,7 @@ class Layer:
     def __init__(self, w: wl.Workload, weights=None):
         self.w = w
         self.host = weights if weights is not None else wl.make_weights(w)
-        d = abi.make_dims(1, w.hidden, w.inter, w.num_experts, w.topk, w.expert_offset)
+        d = abi.make_dims(1, w.hidden, w.inter, w.num_experts, w.topk, w.expert_offset, w.routed_experts)
         raw = [dev(x) for x in self.host]
         self.packed = abi.moe_a8w4_pack_weights(d, *raw)
         torch.cuda.synchronize()
@@ -42,7 +42,8 @@ class Layer:
 
     def dims(self, M):
         w = self.w
-        return abi.make_dims(M, w.hidden, w.inter, w.num_experts, w.topk, w.expert_offset)
+        return abi.make_dims(M, w.hidden, w.inter, w.num_experts, w.topk, w.expert_offset,
+                             w.routed_experts)
 
     def forward(self, hidden, ids, wts, out=None, workspace=None):
         M = hidden.shape[0]

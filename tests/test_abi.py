@@ -83,6 +83,13 @@ def test_block_m_capacity_and_workspace_sizes():
     assert abi.moe_a8w4_block_m(dims(tokens=5)) == 16
     assert abi.moe_a8w4_block_m(dims(tokens=768, num_experts=384, topk=6)) == 32
     assert abi.moe_a8w4_block_m(dims(tokens=16384, num_experts=96, topk=6, inter=2304)) == 128
+    # a 96-expert slice of a 384-expert router: 1024 tokens give 16 routes per expert
+    d = dims(tokens=1024, num_experts=96, topk=6, inter=2304)
+    assert abi.moe_a8w4_block_m(d) == 64          # as if all 6 slots were local
+    d.routed_experts = 384
+    assert abi.moe_a8w4_block_m(d) == 32
+    d.routed_experts = -1
+    assert abi.load().moe_a8w4_block_m(ctypes.byref(d)) == abi.MOE_ERR_DIMS
     d = dims(tokens=33, num_experts=384, topk=6)
     R = 33 * 6
     for bm in (16, 32, 64, 128):

@@ -19,6 +19,7 @@ SMALL = [
     ("draft-sweep", 12, 40, "concentrated"),
     ("backbone-decode", 24, 31, "softmax"),
     ("backbone-decode", 24, 33, "softmax"),
+    ("backbone-decode", 24, 200, "softmax"),
     ("backbone-decode", 24, 257, "softmax"),
     ("local-slice", 8, 16, "softmax"),
     ("prefill-shared", 9, 70, "roundrobin"),
@@ -44,7 +45,8 @@ def test_forward_small_all_tokens(name, E, M, mode):
 
 FULL = [("draft-decode", 5, "softmax"), ("backbone-decode", 768, "softmax"),
         ("backbone-decode", 256, "softmax"), ("draft-sweep", 640, "concentrated"),
-        ("local-slice", 1024, "softmax"), ("local-slice", 16384, "softmax"),
+        ("local-slice", 1024, "softmax"), ("local-slice", 4096, "softmax"),
+        ("local-slice", 16384, "softmax"),
         ("prefill-shared", 4096, "roundrobin"), ("prefill-shared", 16384, "softmax")]
 
 

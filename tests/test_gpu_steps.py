@@ -89,6 +89,28 @@ def test_sort_nonlocal_duplicates_offset_and_repeatability():
     assert int(n.item()) == 0
 
 
+@pytest.mark.parametrize("bm", [16, 128])
+def test_sort_skewed_across_chunks(bm):
+    """Routes are split into chunks sorted by separate workgroups: one expert
+    holding most routes spans all chunks, others are empty or tiny, and some
+    routes are not local."""
+    rng = np.random.default_rng(11)
+    M, k, E, off = 20000, 6, 40, 8
+    ids = rng.integers(0, 64, size=(M, k)).astype(np.int32)
+    hot = rng.random((M, k)) < 0.7
+    ids[hot] = off + 3
+    ids[:, 0] = np.where(rng.random(M) < 0.01, off + E - 1, ids[:, 0])
+    note("sort skewed M=%d bm=%d" % (M, bm))
+    d = abi.make_dims(M, 5120, 640, E, k, off)
+    s, b, n = abi.moe_a8w4_sort(d, bm, dev(ids))
+    torch.cuda.synchronize()
+    rs, rb = oracle.sort(ids, E, off, bm)
+    P = int(n.item())
+    assert P == len(rs)
+    assert np.array_equal(s[:P].cpu().numpy(), rs)
+    assert np.array_equal(b[: P // bm].cpu().numpy(), rb)
+
+
 def test_pack_layout():
     """Packed codes/scales equal the documented permutation of the inputs."""
     E, H, I = 2, 512, 256
