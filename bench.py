@@ -37,6 +37,9 @@ HBM_PEAK_GBS = 8000.0           # MI355X HBM3E, GB/s
 FP8_PEAK_TFLOPS = 5000.0        # dense MFMA, FP8 operands (the A operand here is FP8)
 FP4_PEAK_TFLOPS = 10100.0       # dense MFMA, FP4/FP6 operands
 BUCKETS = (6, 12, 24, 48, 96, 192, 384, 768)
+# A short spin kernel in front of a single timed call keeps host-side launch
+# latency out of its event interval (about 100 us of GPU clock).
+HOST_COVER_CYCLES = 200000
 METRIC = "fused-MoE µs/call per token bucket; HBM GB/s (decode) / MFMA util (prefill)"
 
 
@@ -50,7 +53,68 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run a 1 GiB device copy (reference for HBM byte counters)")
+    ap.add_argument("--local-slice-table", action="store_true",
+                    help="instead of the decode sweep: one call per token count of the local-slice "
+                         "workload (the pages' own MI355X fused_moe timing table) as a JSON line")
     return ap.parse_args()
+
+
+# The pages' MI355X fused_moe call times for the local-slice workload (96 of
+# 384 experts, top-6, H 5120, I 2304, FP8 x MXFP4 per-1x32), tuned lookup,
+# microseconds per call (aiter PR 5904, "Add tuned a8w4 fused-MoE configs for
+# DeepSeek V4.1-Flash (TP4 + EP, gfx950)", kernel benchmark table).  Context
+# only: another software stack, same chip.
+PAGES_LOCAL_SLICE_US = {1: 38.7, 4: 44.9, 16: 94.8, 32: 118.2, 64: 178.1, 128: 269.8, 256: 295.4,
+                        512: 306.8, 1024: 327.5, 2048: 373.7, 4096: 505.2, 8192: 727.8,
+                        16384: 1180.6}
+
+
+def local_slice_table(args):
+    """Median microseconds per moe_a8w4_forward call of the local-slice workload at
+    each token count of the pages' table, with algorithmic GB/s and TFLOP/s."""
+    import torch
+    from mixture_experts_fp8_amd import abi, workloads as wl
+    dev = torch.device("cuda:0")
+    w = wl.WORKLOADS["local-slice"]
+    host_w = wl.make_weights(w)
+    d1 = abi.make_dims(1, w.hidden, w.inter, w.num_experts, w.topk)
+    raw = [torch.from_numpy(np.ascontiguousarray(x)).to(dev) for x in host_w]
+    packed = abi.moe_a8w4_pack_weights(d1, *raw)
+    del raw, host_w
+    rows = {}
+    for M in sorted(PAGES_LOCAL_SLICE_US):
+        hidden, ids, wts = wl.make_inputs(w, M, "softmax")
+        d = abi.make_dims(M, w.hidden, w.inter, w.num_experts, w.topk, w.expert_offset, w.routed_experts)
+        x = torch.from_numpy(hidden.view(np.int16)).to(dev).view(torch.bfloat16)
+        idd = torch.from_numpy(ids).to(dev)
+        wd = torch.from_numpy(wts).to(dev)
+        out = torch.empty((M, w.hidden), dtype=torch.bfloat16, device=dev)
+        ws = torch.empty(abi.moe_a8w4_workspace_bytes(d), dtype=torch.uint8, device=dev)
+        for _ in range(args.warmup):
+            abi.moe_a8w4_forward(d, x, idd, wd, *packed, out=out, workspace=ws)
+        torch.cuda.synchronize()
+        ts = []
+        for _ in range(max(3, args.steps)):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            torch.cuda._sleep(HOST_COVER_CYCLES)   # the GPU waits while the host enqueues the call
+            e0.record()
+            abi.moe_a8w4_forward(d, x, idd, wd, *packed, out=out, workspace=ws)
+            e1.record()
+            e1.synchronize()
+            ts.append(e0.elapsed_time(e1) * 1e3)
+        us = float(np.median(ts))
+        a = algorithmic(w, M, ids)
+        rows[str(M)] = dict(us_per_call=round(us, 1), routes=a["R"], block_m=abi.moe_a8w4_block_m(d),
+                            GBps=round(a["bytes"] / us / 1e3, 1), TFLOPs=round(a["flops"] / us / 1e6, 1),
+                            mfma_frac_fp8_rate=round(a["flops"] / us / 1e6 / FP8_PEAK_TFLOPS, 4),
+                            pages_us=PAGES_LOCAL_SLICE_US[M],
+                            speedup_vs_pages=round(PAGES_LOCAL_SLICE_US[M] / us, 3))
+        print("M=%5d  %8.1f us  (pages %7.1f us)" % (M, us, PAGES_LOCAL_SLICE_US[M]), file=sys.stderr, flush=True)
+    geo = float(np.exp(np.mean([np.log(r["speedup_vs_pages"]) for r in rows.values()])))
+    print(json.dumps({"table": "local-slice fused call, one MI355X", "unit": "us/call",
+                      "config": {"workload": "local slice: H5120, I2304, 96 local of 384 experts, top-6, "
+                                             "softmax routing, MXFP4 weights"},
+                      "rows": rows, "geomean_speedup_vs_pages": round(geo, 3)}))
 
 
 def measured_traffic():
@@ -98,6 +162,9 @@ def main():
     from mixture_experts_fp8_amd import abi, workloads as wl
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
+    if args.local_slice_table:
+        local_slice_table(args)
+        return
     dev = torch.device("cuda:0")
     lib = abi.load()
     w = wl.WORKLOADS["backbone-decode"]
@@ -197,6 +264,7 @@ def main():
         for r in range(reps):
             # another bucket's call in between keeps this bucket's weights out of cache
             call(buckets[(bi + 4) % len(buckets)])
+            torch.cuda._sleep(HOST_COVER_CYCLES)   # the GPU waits while the host enqueues the call
             e0.record(stream)
             if f_fwd(*b["a_fwd"]):
                 raise RuntimeError("moe_a8w4_forward failed")

@@ -1,5 +1,5 @@
 // Grouped GEMMs of the A8W4 MoE layer on the gfx950 scaled F8F6F4 MFMA, for
-// decode-sized blocks (block_m 16 .. 64); larger blocks use gemm_tile.hip.
+// decode-sized blocks (block_m 16 and 32); larger blocks use gemm_tile.hip.
 //
 // Stage one: for each block of sorted routes of expert e, gate/up rows of
 // w13[e] (MXFP4, interleaved: row 2j gate j, row 2j+1 up j) times the routed
@@ -82,6 +82,20 @@ __global__ void __launch_bounds__(256) gemm_kernel(GemmArgs args) {
     const int64_t row = (STAGE == 1) ? (int64_t)(rid[c] & 0xFFFFFF) : (int64_t)b * bm + c * 16 + t16;
     brow[c] = args.bq + row * K + 16 * g;
     bsrow[c] = args.bs + row * (K / 32) + g;
+  }
+
+  // stage two: the routes' slots and routing weights, fetched before the K
+  // loop so the epilogue does not wait for them
+  int64_t slot[NCG];
+  float wt[NCG];
+#pragma unroll
+  for (int c = 0; c < NCG; ++c) {
+    slot[c] = 0;
+    wt[c] = 0.f;
+    if (STAGE == 2 && valid[c]) {
+      slot[c] = route_slot(rid[c], args.topk);
+      wt[c] = args.topk_weights[slot[c]];
+    }
   }
 
   const uint8_t* wp = args.w + (int64_t)e * ((int64_t)N * K / 2) + (int64_t)grp * KS * 4096 + lane * 16;
@@ -171,7 +185,7 @@ __global__ void __launch_bounds__(256) gemm_kernel(GemmArgs args) {
       if constexpr (STAGE == 1)
         stage1_store(part, (int64_t)b * bm + c * 16 + t16, grp, N / 2, g, args.out_q, args.out_s);
       else if (valid[c])
-        stage2_store(part, rid[c], args, grp, g);
+        stage2_store(part, slot[c], wt[c], args, grp, g);
     }
   }
 }
@@ -198,31 +212,26 @@ hipError_t launch_gemm(const GemmArgs& a, int64_t max_blocks, hipStream_t stream
 #ifndef MOE_NT_SMALL
 #define MOE_NT_SMALL true
 #endif
-// smallest block size that goes to the LDS-tiled kernel of gemm_tile.hip
-#ifndef MOE_TILE_MIN_BM
-#define MOE_TILE_MIN_BM 64
-#endif
 
 }  // namespace
 
+// Blocks of 16 or 32 routes run here; 64 and 128 go to the LDS-tiled kernel.
 hipError_t launch_stage1(const GemmArgs& a, int64_t max_blocks, hipStream_t stream) {
-  if (a.bm >= MOE_TILE_MIN_BM) return launch_tile(1, a, max_blocks, stream);
   switch (a.bm) {
     case 16: return launch_gemm<1, 1, MOE_S1_NWK_SMALL, MOE_S1_PD, MOE_NT_SMALL>(a, max_blocks, stream);
     case 32: return launch_gemm<1, 2, MOE_S1_NWK_SMALL, MOE_S1_PD, MOE_NT_SMALL>(a, max_blocks, stream);
-    case 64: return launch_gemm<1, 4, MOE_S1_NWK_SMALL, MOE_S1_PD, MOE_NT_SMALL>(a, max_blocks, stream);
-    case 128: return launch_gemm<1, 8, 1, 2, false>(a, max_blocks, stream);
+    case 64:
+    case 128: return launch_tile(1, a, max_blocks, stream);
     default: return hipErrorInvalidValue;
   }
 }
 
 hipError_t launch_stage2(const GemmArgs& a, int64_t max_blocks, hipStream_t stream) {
-  if (a.bm >= MOE_TILE_MIN_BM) return launch_tile(2, a, max_blocks, stream);
   switch (a.bm) {
     case 16: return launch_gemm<2, 1, 1, MOE_S2_PD, MOE_NT_SMALL>(a, max_blocks, stream);
     case 32: return launch_gemm<2, 2, 1, MOE_S2_PD, MOE_NT_SMALL>(a, max_blocks, stream);
-    case 64: return launch_gemm<2, 4, 1, MOE_S2_PD, MOE_NT_SMALL>(a, max_blocks, stream);
-    case 128: return launch_gemm<2, 8, 1, 2, false>(a, max_blocks, stream);
+    case 64:
+    case 128: return launch_tile(2, a, max_blocks, stream);
     default: return hipErrorInvalidValue;
   }
 }

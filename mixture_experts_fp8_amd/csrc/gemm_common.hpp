@@ -48,7 +48,9 @@ __device__ __forceinline__ void stage1_store(const v4f acc[4], int64_t p, int gr
 #pragma unroll
     for (int q = 0; q < 2; ++q) {
       const float gate = acc[t][2 * q], up = acc[t][2 * q + 1];
-      h[2 * t + q] = gate / (1.0f + __expf(-gate)) * up;
+      // SiLU with the hardware reciprocal (about 1 ulp): the result is
+      // rounded to 3 mantissa bits right after
+      h[2 * t + q] = gate * __builtin_amdgcn_rcpf(1.0f + __expf(-gate)) * up;
     }
   float amax = 0.f;
 #pragma unroll
@@ -60,16 +62,19 @@ __device__ __forceinline__ void stage1_store(const v4f acc[4], int64_t p, int gr
   if (g == 0) out_s[p * (I / 32) + grp] = (uint8_t)(E + 127);
 }
 
+// Route slot t * topk + k of a sorted id.
+__device__ __forceinline__ int64_t route_slot(int rid, int topk) {
+  return (int64_t)(rid & 0xFFFFFF) * topk + (rid >> kSentinelShift);
+}
+
 // Stage-two epilogue: lane (t16, g) holds output columns 64 grp + 16g + 4t + r
-// of one route; writes topk_weight * value to that route's row, 16 consecutive
-// floats per lane (the four lanes of a route write 256 B in a row).  The rows
-// stay in float32: routes of one token can cancel, and a BF16 rounding of
-// each route's share would then exceed the output tolerance.
-__device__ __forceinline__ void stage2_store(const v4f acc[4], int rid, const GemmArgs& args,
+// of the route in slot `slot`; writes wt * value (wt its routing weight) to
+// that route's row, 16 consecutive floats per lane (the four lanes of a route
+// write 256 B in a row).  The rows stay in float32: routes of one token can
+// cancel, and a BF16 rounding of each route's share would then exceed the
+// output tolerance.
+__device__ __forceinline__ void stage2_store(const v4f acc[4], int64_t slot, float wt, const GemmArgs& args,
                                              int grp, int g) {
-  const int tok = rid & 0xFFFFFF, k = rid >> kSentinelShift;
-  const int64_t slot = (int64_t)tok * args.topk + k;
-  const float wt = args.topk_weights[slot];
   float4* dst = reinterpret_cast<float4*>(args.y_routes + slot * args.N + grp * 64 + 16 * g);
 #pragma unroll
   for (int t = 0; t < 4; ++t)

@@ -5,15 +5,19 @@
 // weight and per-route rows; aiter PR 5609, "Add DeepSeek V4.1 Flash TP4
 // gfx950 MoE tuning", Configuration), organised for operand reuse:
 //
-//   workgroup tile  256 weight rows x BM tokens (BM = 32 CGW), 4 waves as
-//                   2 x 2: wave (wr, wc) computes rows [128 wr, +128) (two
-//                   64-row groups, 8 MFMA tiles) x tokens [wc BM/2, +BM/2)
+//   workgroup tile  256 weight rows x BM tokens (BM = 32 CGW)
+//   waves           8 compute waves as 4 x 2: wave (wr, wc) computes rows
+//                   [64 wr, +64) (one 64-row group, 4 MFMA tiles) x tokens
+//                   [wc BM/2, +BM/2); and 4 loader waves that only move data.
+//                   Each SIMD runs two compute waves (one hides the other's
+//                   LDS reads and barrier waits) and one loader (a loader
+//                   stalled on the memory pipeline never holds back MFMAs).
 //   K step          128: 16 KB of packed weights, BM x 128 B of token codes,
 //                   1 KB of weight scales and BM x 4 B of token scales
 //   staging         a ring of S such steps in LDS, filled by direct
-//                   global-to-LDS loads (no registers involved), S - 1 steps
-//                   in flight while the MFMAs consume one; one barrier per
-//                   step.
+//                   global-to-LDS loads (no registers involved): while the
+//                   MFMAs consume step s, steps s + 1 .. s + S - 1 are in
+//                   flight; one workgroup barrier per step.
 //
 // LDS layout of one step (offsets in bytes):
 //   A   [4 row groups][4 tiles][64 lanes][16]   the packed chunk as stored
@@ -22,14 +26,15 @@
 //                                               lanes of one operand read hit 16
 //                                               distinct 16-byte bank slots
 //   As  [4 row groups][64 lanes][4]             E8M0 weight scales
-//   Bs  [4 copies][64 tokens][4]                E8M0 token scales; wave w loads
-//                                               tokens 64 (w mod BM/64) + lane,
-//                                               so tokens 0..BM-1 sit in order
-//                                               at the start of the area
+//   Bs  [4 copies][64 tokens][4]                E8M0 token scales; loader l
+//                                               loads tokens 64 (l mod BM/64) +
+//                                               lane, so tokens 0..BM-1 sit in
+//                                               order at the start of the area
 //
-// Each wave issues the same number of loads per step, so one vmcnt value
-// tells every wave that its share of a step has landed; the barrier then
-// publishes all shares and frees the slot that was read one step earlier.
+// Barrier s: every loader has waited until its loads of step s have landed
+// (vmcnt), every compute wave until its LDS reads of step s - 1 are done.  It
+// publishes step s and frees the slot of step s - 1, which the loaders refill
+// with step s + S - 1 while the compute waves work on step s.
 #include "gemm_common.hpp"
 
 namespace moe {
@@ -47,8 +52,23 @@ typedef __attribute__((address_space(3))) void* lds_ptr;
 // assembly so that the compiler, which cannot tell the ring's slots apart,
 // does not wait for every load in flight before each LDS read; the kernel
 // waits for them itself (vmcnt) before the barrier that publishes a slot.
+#ifndef MOE_TILE_AMOD
+#define MOE_TILE_AMOD ""
+#endif
+#ifndef MOE_TILE_BMOD
+#define MOE_TILE_BMOD ""
+#endif
 __device__ __forceinline__ void dma16(const void* g, uint32_t lds) {
   asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(g), "s"(lds)
+               : "memory", "m0");
+}
+// the same with cache-policy bits appended (weights stream once per slice)
+__device__ __forceinline__ void dma16_a(const void* g, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off " MOE_TILE_AMOD ::"v"(g), "s"(lds)
+               : "memory", "m0");
+}
+__device__ __forceinline__ void dma16_b(const void* g, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off " MOE_TILE_BMOD ::"v"(g), "s"(lds)
                : "memory", "m0");
 }
 __device__ __forceinline__ void dma4(const void* g, uint32_t lds) {
@@ -61,13 +81,14 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
 
 template <int CGW>
 struct TileGeom {
-  static constexpr int BM = 32 * CGW;
+  static constexpr int BM = 32 * CGW;               // tokens
+  static constexpr int NBCH = CGW;                  // 1 KB token chunks per loader and step
   static constexpr int A = 0;
-  static constexpr int B = 16384;
+  static constexpr int B = A + 16384;
   static constexpr int AS = B + BM * 128;
   static constexpr int BS = AS + 1024;
   static constexpr int BYTES = BS + 1024;
-  static constexpr int LOADS = 4 + CGW + 2;   // per wave and step: A, B chunks, As, Bs
+  static constexpr int LOADS = 4 + NBCH + 2;        // per loader and step: A, B chunks, As, Bs
 };
 
 // s_waitcnt immediates (gfx9 encoding): wait on the vector-memory counter
@@ -86,7 +107,7 @@ __device__ __forceinline__ void barrier_only() {
 // Tile order.  In block-major order (t = b NT + wgt) the tiles of one expert
 // form the run [f NT, (f + nb) NT), f its first block and nb its block count.
 // Inside that run the tiles are taken slice-major (wgt = l / nb, b = f + l % nb)
-// so that the nb blocks that read the same 256-row weight slice run side by
+// so that the nb blocks that read the same weight slice run side by
 // side on one XCD and share it through its L2, while the expert's token
 // blocks stay resident there across the slices.  f and nb come from the run
 // of equal entries of block_expert around block t / NT (every wave finds
@@ -120,8 +141,10 @@ __device__ __forceinline__ void expert_major(int t, int NT, int nblk, const int3
   b = f + (l - wgt * nb);
 }
 
-template <int STAGE, int CGW, int S, int WPE>
-__global__ void __launch_bounds__(256, WPE) tile_kernel(GemmArgs args) {
+constexpr int kComputeWaves = 8, kLoaderWaves = 4;
+
+template <int STAGE, int CGW, int S>
+__global__ void __launch_bounds__(64 * (kComputeWaves + kLoaderWaves), 3) tile_kernel(GemmArgs args) {
   using G = TileGeom<CGW>;
   constexpr int BM = G::BM;
   __shared__ __attribute__((aligned(1024))) uint8_t smem[S][G::BYTES];
@@ -134,85 +157,101 @@ __global__ void __launch_bounds__(256, WPE) tile_kernel(GemmArgs args) {
   if ((int)blockIdx.x >= T) return;
   int b, wgt;
   expert_major(xcd_tile(blockIdx.x, T), NT, nblk, args.block_expert, b, wgt);
-  const int e = args.block_expert[b];
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform: LDS bases go to M0
-  const int wr = wave >> 1, wc = wave & 1;
-  const int t16 = lane & 15, g = lane >> 4;
   const int32_t* ids = args.sorted_ids + (int64_t)b * BM;
-  const int first = ids[0];   // a block always starts with a route
 
-  // B row of block token t; padding tokens read a real row (their columns
-  // are never stored, the load only has to stay in bounds)
-  auto brow = [&](int t) -> int64_t {
-    if (STAGE == 1) {
-      const int r = ids[t];
-      return (int64_t)((r == M ? first : r) & 0xFFFFFF);
+  if (wave >= kComputeWaves) {
+    // ------------------------------------------------------------ loader
+    const int l = wave - kComputeWaves;
+    const int e = args.block_expert[b];
+    const int first = ids[0];   // a block always starts with a route
+    // B row of block token t; padding tokens read a real row (their
+    // columns are never stored, the load only has to stay in bounds)
+    auto brow = [&](int t) -> int64_t {
+      if (STAGE == 1) {
+        const int r = ids[t];
+        return (int64_t)((r == M ? first : r) & 0xFFFFFF);
+      }
+      return (int64_t)b * BM + t;
+    };
+    const uint8_t* gA = args.w + (int64_t)e * ((int64_t)N * K / 2) +
+                        (int64_t)(wgt * 4 + l) * KS * 4096 + lane * 16;
+    const uint8_t* gAs = args.ws + (int64_t)e * ((int64_t)N * K / 32) +
+                         (int64_t)(wgt * 4 + l) * KS * 256 + lane * 4;
+    const uint8_t* gB[G::NBCH];
+#pragma unroll
+    for (int i = 0; i < G::NBCH; ++i) {
+      const int t = 8 * (l * G::NBCH + i) + (lane >> 3);
+      const int piece = (lane & 7) ^ ((t >> 1) & 7);
+      gB[i] = args.bq + brow(t) * K + piece * 16;
     }
-    return (int64_t)b * BM + t;
-  };
-
-  // per-lane global sources of this wave's loads, at step 0
-  const uint8_t* gA = args.w + (int64_t)e * ((int64_t)N * K / 2) +
-                      (int64_t)(wgt * 4 + wave) * KS * 4096 + lane * 16;
-  const uint8_t* gAs = args.ws + (int64_t)e * ((int64_t)N * K / 32) +
-                       (int64_t)(wgt * 4 + wave) * KS * 256 + lane * 4;
-  const uint8_t* gB[CGW];
-#pragma unroll
-  for (int i = 0; i < CGW; ++i) {
-    const int t = 8 * (wave * CGW + i) + (lane >> 3);
-    const int piece = (lane & 7) ^ ((t >> 1) & 7);
-    gB[i] = args.bq + brow(t) * K + piece * 16;
-  }
-  constexpr int NBS = BM / 64;
-  const uint8_t* gBs = args.bs + brow((wave % NBS) * 64 + lane) * (K / 32);
-
-  const uint32_t lds0 = lds_addr(&smem[0][0]);
-  auto issue = [&](int s) {
-    const uint32_t base = lds0 + (uint32_t)(s % S) * G::BYTES;
-#pragma unroll
-    for (int t = 0; t < 4; ++t) dma16(gA + (int64_t)s * 4096 + t * 1024, base + G::A + wave * 4096 + t * 1024);
-#pragma unroll
-    for (int i = 0; i < CGW; ++i) dma16(gB[i] + s * 128, base + G::B + (wave * CGW + i) * 1024);
-    dma4(gAs + (int64_t)s * 256, base + G::AS + wave * 256);
-    dma4(gBs + 4 * s, base + G::BS + wave * 256);
-  };
-
-  // the K loop and epilogue for NA active 16-token column groups of this
-  // wave (columns past the block's last route are skipped); every wave takes
-  // its share of the loads and every barrier whatever its NA
-  auto run = [&](auto na_tag) {
-    constexpr int NA = decltype(na_tag)::value;
-    v4f acc[2][4][NA > 0 ? NA : 1];
-#pragma unroll
-    for (int rg = 0; rg < 2; ++rg)
+    constexpr int NBS = BM / 64;
+    const uint8_t* gBs = args.bs + brow((l % NBS) * 64 + lane) * (K / 32);
+    const uint32_t lds0 = lds_addr(&smem[0][0]);
+    auto issue = [&](int s) {
+      const uint32_t base = lds0 + (uint32_t)(s % S) * G::BYTES;
 #pragma unroll
       for (int t = 0; t < 4; ++t)
+        dma16_a(gA + (int64_t)s * 4096 + t * 1024, base + G::A + l * 4096 + t * 1024);
 #pragma unroll
-        for (int c = 0; c < NA; ++c) acc[rg][t][c] = v4f{0.f, 0.f, 0.f, 0.f};
-
+      for (int i = 0; i < G::NBCH; ++i) dma16_b(gB[i] + s * 128, base + G::B + (l * G::NBCH + i) * 1024);
+      dma4(gAs + (int64_t)s * 256, base + G::AS + l * 256);
+      dma4(gBs + 4 * s, base + G::BS + l * 256);
+    };
 #pragma unroll
     for (int s = 0; s < S - 1; ++s)
       if (s < KS) issue(s);
     for (int s = 0; s < KS; ++s) {
-      // this wave's loads of step s have landed once at most the loads of
-      // the steps after it are outstanding
+      // barrier s publishes step s: it has landed once at most the loads of
+      // steps s+1 .. s+S-2 are outstanding (near the end: none)
       if (s + S - 2 < KS) __builtin_amdgcn_s_waitcnt(vmcnt_only((S - 2) * G::LOADS));
       else __builtin_amdgcn_s_waitcnt(vmcnt_only(0));
-      __builtin_amdgcn_s_waitcnt(lgkmcnt_zero());   // this wave's reads of step s - 1 are done
       barrier_only();
+      // every compute wave has finished reading step s - 1: refill its slot
       if (s + S - 1 < KS) issue(s + S - 1);
+    }
+    return;
+  }
+
+  // -------------------------------------------------------------- compute
+  const int wr = wave >> 1, wc = wave & 1;
+  const int t16 = lane & 15, g = lane >> 4;
+
+  // the K loop and epilogue for NA active 16-token column groups of this
+  // wave (columns past the block's last route are skipped); every compute
+  // wave takes every barrier whatever its NA
+  auto run = [&](auto na_tag) {
+    constexpr int NA = decltype(na_tag)::value;
+    // stage two: slots and routing weights of this wave's columns, fetched
+    // before the K loop so the epilogue does not wait for them
+    int64_t slot[NA > 0 ? NA : 1];
+    float wt[NA > 0 ? NA : 1];
+    if constexpr (STAGE == 2) {
+#pragma unroll
+      for (int c = 0; c < NA; ++c) {
+        const int rid = ids[wc * CGW * 16 + c * 16 + t16];
+        slot[c] = rid == M ? -1 : route_slot(rid, args.topk);
+        wt[c] = rid == M ? 0.f : args.topk_weights[slot[c]];
+      }
+    }
+    v4f acc[4][NA > 0 ? NA : 1];
+#pragma unroll
+    for (int t = 0; t < 4; ++t)
+#pragma unroll
+      for (int c = 0; c < NA; ++c) acc[t][c] = v4f{0.f, 0.f, 0.f, 0.f};
+
+    for (int s = 0; s < KS; ++s) {
+      // this wave's reads of step s - 1 are done; barrier s publishes step s
+      __builtin_amdgcn_s_waitcnt(lgkmcnt_zero());
+      barrier_only();
       if constexpr (NA > 0) {
         const uint8_t* base = smem[s % S];
-        v4i a[2][4];
-        uint32_t sa[2];
+        v4i a[4];
 #pragma unroll
-        for (int rg = 0; rg < 2; ++rg) {
-#pragma unroll
-          for (int t = 0; t < 4; ++t)
-            a[rg][t] = *reinterpret_cast<const v4i*>(base + G::A + (2 * wr + rg) * 4096 + t * 1024 + lane * 16);
-          sa[rg] = *reinterpret_cast<const uint32_t*>(base + G::AS + (2 * wr + rg) * 256 + lane * 4);
-        }
+        for (int t = 0; t < 4; ++t)
+          a[t] = *reinterpret_cast<const v4i*>(base + G::A + wr * 4096 + t * 1024 + lane * 16);
+        const uint32_t sa = *reinterpret_cast<const uint32_t*>(base + G::AS + wr * 256 + lane * 4);
 #pragma unroll
         for (int c = 0; c < NA; ++c) {
           const int tok = wc * CGW * 16 + c * 16 + t16;
@@ -221,30 +260,23 @@ __global__ void __launch_bounds__(256, WPE) tile_kernel(GemmArgs args) {
           const v8i bb = join8(*reinterpret_cast<const v4i*>(row + ((g ^ sw) << 4)),
                                *reinterpret_cast<const v4i*>(row + (((4 + g) ^ sw) << 4)));
           const uint32_t sb = (*reinterpret_cast<const uint32_t*>(base + G::BS + tok * 4) >> (8 * g)) & 0xFFu;
-#pragma unroll
-          for (int rg = 0; rg < 2; ++rg) {
-            acc[rg][0][c] = mfma_fp4_fp8<0>(a[rg][0], bb, acc[rg][0][c], sa[rg], sb);
-            acc[rg][1][c] = mfma_fp4_fp8<1>(a[rg][1], bb, acc[rg][1][c], sa[rg], sb);
-            acc[rg][2][c] = mfma_fp4_fp8<2>(a[rg][2], bb, acc[rg][2][c], sa[rg], sb);
-            acc[rg][3][c] = mfma_fp4_fp8<3>(a[rg][3], bb, acc[rg][3][c], sa[rg], sb);
-          }
+          acc[0][c] = mfma_fp4_fp8<0>(a[0], bb, acc[0][c], sa, sb);
+          acc[1][c] = mfma_fp4_fp8<1>(a[1], bb, acc[1][c], sa, sb);
+          acc[2][c] = mfma_fp4_fp8<2>(a[2], bb, acc[2][c], sa, sb);
+          acc[3][c] = mfma_fp4_fp8<3>(a[3], bb, acc[3][c], sa, sb);
         }
       }
     }
 
+    const int grp = wgt * 4 + wr;
 #pragma unroll
-    for (int rg = 0; rg < 2; ++rg) {
-      const int grp = wgt * 4 + 2 * wr + rg;
-#pragma unroll
-      for (int c = 0; c < NA; ++c) {
-        const v4f part[4] = {acc[rg][0][c], acc[rg][1][c], acc[rg][2][c], acc[rg][3][c]};
-        const int col = wc * CGW * 16 + c * 16 + t16;
-        if constexpr (STAGE == 1) {
-          stage1_store(part, (int64_t)b * BM + col, grp, N / 2, g, args.out_q, args.out_s);
-        } else {
-          const int rid = ids[col];
-          if (rid != M) stage2_store(part, rid, args, grp, g);
-        }
+    for (int c = 0; c < NA; ++c) {
+      const v4f part[4] = {acc[0][c], acc[1][c], acc[2][c], acc[3][c]};
+      const int col = wc * CGW * 16 + c * 16 + t16;
+      if constexpr (STAGE == 1) {
+        stage1_store(part, (int64_t)b * BM + col, grp, N / 2, g, args.out_q, args.out_s);
+      } else if (slot[c] >= 0) {
+        stage2_store(part, slot[c], wt[c], args, grp, g);
       }
     }
   };
@@ -263,26 +295,22 @@ __global__ void __launch_bounds__(256, WPE) tile_kernel(GemmArgs args) {
   }
 }
 
-// ring depth and waves per SIMD: 2 steps and 2 workgroups per CU (69.6 KB of
-// LDS each at BM = 128), or 3 steps and one
 #ifndef MOE_TILE_STAGES
-#define MOE_TILE_STAGES 2
+#define MOE_TILE_STAGES 3
 #endif
-#ifndef MOE_TILE_WPE
-#define MOE_TILE_WPE 2
-#endif
+static_assert(MOE_TILE_STAGES >= 2, "the ring holds the step in use and at least one in flight");
 
 }  // namespace
 
 hipError_t launch_tile(int stage, const GemmArgs& a, int64_t max_blocks, hipStream_t stream) {
-  constexpr int S = MOE_TILE_STAGES, W = MOE_TILE_WPE;
+  constexpr int S = MOE_TILE_STAGES;
   const int64_t grid = max_blocks * (a.N / 256);
   if (grid <= 0) return hipSuccess;
-  const dim3 g((unsigned)grid), blk(256);
-  if (stage == 1 && a.bm == 128) hipLaunchKernelGGL((tile_kernel<1, 4, S, W>), g, blk, 0, stream, a);
-  else if (stage == 1 && a.bm == 64) hipLaunchKernelGGL((tile_kernel<1, 2, S, W>), g, blk, 0, stream, a);
-  else if (stage == 2 && a.bm == 128) hipLaunchKernelGGL((tile_kernel<2, 4, S, W>), g, blk, 0, stream, a);
-  else if (stage == 2 && a.bm == 64) hipLaunchKernelGGL((tile_kernel<2, 2, S, W>), g, blk, 0, stream, a);
+  const dim3 g((unsigned)grid), blk(64 * (kComputeWaves + kLoaderWaves));
+  if (stage == 1 && a.bm == 128) hipLaunchKernelGGL((tile_kernel<1, 4, S>), g, blk, 0, stream, a);
+  else if (stage == 1 && a.bm == 64) hipLaunchKernelGGL((tile_kernel<1, 2, S>), g, blk, 0, stream, a);
+  else if (stage == 2 && a.bm == 128) hipLaunchKernelGGL((tile_kernel<2, 4, S>), g, blk, 0, stream, a);
+  else if (stage == 2 && a.bm == 64) hipLaunchKernelGGL((tile_kernel<2, 2, S>), g, blk, 0, stream, a);
   else return hipErrorInvalidValue;
   return hipGetLastError();
 }
