@@ -141,7 +141,9 @@ __global__ void __launch_bounds__(256) gemm_kernel(GemmArgs args) {
   };
 
   // software pipeline: a ring of PD fragments, loads issued PD - 1 steps ahead
-  const int s0 = wk * (KS / NWK), s1 = s0 + KS / NWK;
+  // wave wk of a row group takes steps [wk KS / NWK, (wk + 1) KS / NWK): all
+  // KS steps for any KS (a wave may get none when KS < NWK)
+  const int s0 = wk * KS / NWK, s1 = (wk + 1) * KS / NWK;
   Frag<NCG> f[PD];
 #pragma unroll
   for (int u = 0; u < PD - 1; ++u)
