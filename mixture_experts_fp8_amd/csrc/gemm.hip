@@ -180,14 +180,22 @@ __global__ void __launch_bounds__(256) gemm_kernel(GemmArgs args) {
           for (int r = 0; r < 4; ++r) acc[t][c][r] += red[p * NWR + wr][t][c][r][lane];
   }
 
+  if constexpr (STAGE == 1) {
 #pragma unroll
-  for (int c = 0; c < NCG; ++c) {
-    if (c < nact) {
-      const v4f part[4] = {acc[0][c], acc[1][c], acc[2][c], acc[3][c]};
-      if constexpr (STAGE == 1)
+    for (int c = 0; c < NCG; ++c) {
+      if (c < nact) {
+        const v4f part[4] = {acc[0][c], acc[1][c], acc[2][c], acc[3][c]};
         stage1_store(part, (int64_t)b * bm + c * 16 + t16, grp, N / 2, g, args.out_q, args.out_s);
-      else if (valid[c])
-        stage2_store(part, slot[c], wt[c], args, grp, g);
+      }
+    }
+  } else {
+    __shared__ __attribute__((aligned(16))) uint8_t scr[4][kStage2Scratch];   // one area per wave
+#pragma unroll
+    for (int c = 0; c < NCG; ++c) {
+      if (c < nact) {
+        const v4f part[4] = {acc[0][c], acc[1][c], acc[2][c], acc[3][c]};
+        stage2_store(part, valid[c] ? slot[c] : -1, wt[c], args, grp, g, scr[wave]);
+      }
     }
   }
 }

@@ -67,18 +67,44 @@ __device__ __forceinline__ int64_t route_slot(int rid, int topk) {
   return (int64_t)(rid & 0xFFFFFF) * topk + (rid >> kSentinelShift);
 }
 
-// Stage-two epilogue: lane (t16, g) holds output columns 64 grp + 16g + 4t + r
-// of the route in slot `slot`; writes wt * value (wt its routing weight) to
-// that route's row, 16 consecutive floats per lane (the four lanes of a route
-// write 256 B in a row).  The rows stay in float32: routes of one token can
-// cancel, and a BF16 rounding of each route's share would then exceed the
-// output tolerance.
+// Orders one wave's LDS writes before its following LDS reads (and the
+// reverse): the lanes of a wave run in lockstep, the fences make the compiler
+// keep the order and wait for the outstanding LDS operations.
+__device__ __forceinline__ void wave_lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+// Bytes of wave-private LDS scratch stage2_store needs.
+constexpr int kStage2Scratch = 16 * 272;
+
+// Stage-two epilogue for one 64-row group and one 16-route column group of a
+// wave: lane (t16, g) holds output columns 64 grp + 16g + 4t + r of the route
+// in slot `slot` (negative: no route), wt its routing weight.  The rows
+// wt * value are written to that route's row of y_routes (float32; routes of
+// one token can cancel, and a BF16 rounding of each route's share would then
+// exceed the output tolerance).  They go through the wave's LDS scratch
+// (16 rows of 256 B, padded to 272 against bank conflicts) so that each store
+// instruction writes 4 routes x 256 B in a row instead of 16-byte pieces of 16
+// routes.  All 64 lanes must call it together.
 __device__ __forceinline__ void stage2_store(const v4f acc[4], int64_t slot, float wt, const GemmArgs& args,
-                                             int grp, int g) {
-  float4* dst = reinterpret_cast<float4*>(args.y_routes + slot * args.N + grp * 64 + 16 * g);
+                                             int grp, int g, uint8_t* scr) {
+  const int lane = threadIdx.x & 63, t16 = lane & 15;
 #pragma unroll
   for (int t = 0; t < 4; ++t)
-    dst[t] = make_float4(wt * acc[t][0], wt * acc[t][1], wt * acc[t][2], wt * acc[t][3]);
+    *reinterpret_cast<v4f*>(scr + t16 * 272 + (16 * g + 4 * t) * 4) =
+        v4f{wt * acc[t][0], wt * acc[t][1], wt * acc[t][2], wt * acc[t][3]};
+  wave_lds_sync();
+  const int slo = (int)(uint32_t)slot, shi = (int)(slot >> 32);
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int route = 4 * q + (lane >> 4), chunk = lane & 15;
+    const int64_t sl = ((int64_t)__shfl(shi, route) << 32) | (uint32_t)__shfl(slo, route);
+    const v4f v = *reinterpret_cast<const v4f*>(scr + route * 272 + chunk * 16);
+    if (sl >= 0) *reinterpret_cast<v4f*>(args.y_routes + sl * args.N + grp * 64 + chunk * 4) = v;
+  }
+  wave_lds_sync();
 }
 
 }  // namespace moe

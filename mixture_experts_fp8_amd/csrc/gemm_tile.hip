@@ -96,15 +96,6 @@ struct TileGeom {
 constexpr int vmcnt_only(int n) { return (n & 15) | (((n >> 4) & 3) << 14) | (7 << 4) | (15 << 8); }
 constexpr int lgkmcnt_zero() { return 15 | (3 << 14) | (7 << 4); }
 
-// Orders one wave's LDS writes before its following LDS reads (and the
-// reverse): the lanes of a wave run in lockstep, the fences make the compiler
-// keep the order and wait for the outstanding LDS operations.
-__device__ __forceinline__ void wave_lds_sync() {
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-  __builtin_amdgcn_wave_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-}
-
 // A workgroup barrier without the memory fences of __syncthreads (those would
 // also wait for every direct-to-LDS load still in flight).
 __device__ __forceinline__ void barrier_only() {
@@ -286,30 +277,14 @@ __global__ void __launch_bounds__(64 * (kComputeWaves + kLoaderWaves), 3) tile_k
         stage1_store(part, (int64_t)b * BM + col, grp, N / 2, g, args.out_q, args.out_s);
       }
     } else {
-      // Weighted route rows go out through LDS so that each store writes 4
-      // routes x 256 B in a row (the MFMA layout would scatter 16-byte pieces
-      // over 16 routes).  Scratch: a wave-private 16 x 272-byte area (rows
-      // padded by 16 B against bank conflicts) in one of the two ring slots
-      // no wave touches after the last barrier (the slots of steps KS - 3 and
-      // KS - 2, or unused ones).
-      uint8_t* scr = smem[(KS + (wave >> 2)) % S] + (wave & 3) * (16 * 272);
+      // the route rows go out through LDS scratch: a wave-private area in
+      // one of the two ring slots no wave touches after the last barrier
+      // (the slots of steps KS - 3 and KS - 2, or unused ones)
+      uint8_t* scr = smem[(KS + (wave >> 2)) % S] + (wave & 3) * kStage2Scratch;
 #pragma unroll
       for (int c = 0; c < NA; ++c) {
-        const float w_ = wt[c];
-#pragma unroll
-        for (int t = 0; t < 4; ++t)
-          *reinterpret_cast<v4f*>(scr + t16 * 272 + (16 * g + 4 * t) * 4) =
-              v4f{w_ * acc[t][c][0], w_ * acc[t][c][1], w_ * acc[t][c][2], w_ * acc[t][c][3]};
-        wave_lds_sync();
-        const int slo = (int)(uint32_t)slot[c], shi = (int)(slot[c] >> 32);
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const int route = 4 * q + (lane >> 4), chunk = lane & 15;
-          const int64_t sl = ((int64_t)__shfl(shi, route) << 32) | (uint32_t)__shfl(slo, route);
-          const v4f v = *reinterpret_cast<const v4f*>(scr + route * 272 + chunk * 16);
-          if (sl >= 0) *reinterpret_cast<v4f*>(args.y_routes + sl * N + grp * 64 + chunk * 4) = v;
-        }
-        wave_lds_sync();
+        const v4f part[4] = {acc[0][c], acc[1][c], acc[2][c], acc[3][c]};
+        stage2_store(part, slot[c], wt[c], args, grp, g, scr);
       }
     }
   };
