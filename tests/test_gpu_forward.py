@@ -93,6 +93,30 @@ def test_forward_full_size_sampled(layers, name, M, mode):
     assert np.array_equal(wd.cpu().numpy(), wts)
 
 
+TILE_SHAPES = [  # (hidden, inter, experts, topk, tokens): block_m 64/128 with short and odd K
+    (512, 128, 4, 2, 300),    # stage two has a single K step
+    (1024, 384, 3, 1, 200),   # stage two has three K steps (ring of three)
+    (512, 256, 8, 2, 200),    # block_m 64, two K steps in stage two
+]
+
+
+@pytest.mark.parametrize("H,I,E,k,M", TILE_SHAPES)
+def test_tile_kernel_short_and_odd_k(H, I, E, k, M):
+    base = wl.WORKLOADS["draft-decode"]
+    w = wl.scaled(base, hidden=H, inter=I, inter_valid=I, num_experts=E, routed_experts=E, topk=k,
+                  config_id=200 + H + I + E)
+    layer = Layer(w)
+    hidden, ids, wts = wl.make_inputs(w, M, "softmax")
+    bm = abi.moe_a8w4_block_m(layer.dims(M))
+    assert bm >= 64
+    note("tile kernel H=%d I=%d E=%d k=%d M=%d bm=%d" % (H, I, E, k, M, bm))
+    out = torch.full((M, w.hidden), float("nan"), dtype=torch.bfloat16, device=DEV)
+    xd, idd = dev(hidden), dev(ids)
+    layer.forward(xd, idd, wts, out=out)
+    torch.cuda.synchronize()
+    check_forward(layer, hidden, ids, wts, host_bf16_bits(out), xd, idd)
+
+
 def test_edge_cases():
     w = wl.scaled(wl.WORKLOADS["backbone-decode"], num_experts=12, routed_experts=12, config_id=120)
     layer = Layer(w)
