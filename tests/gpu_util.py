@@ -167,7 +167,7 @@ def check_intermediate(layer, hidden, ids, routes, giq, gis):
         hb = (np.abs(h) + budget).reshape(h.shape[0], -1, 32).max(axis=2)
         lo = np.maximum(np.abs(h) - budget, 0).reshape(h.shape[0], -1, 32).max(axis=2)
         # a power of two must lie within [lo, hb] of the exact block maximum
-        crosses = np.floor(np.log2(np.maximum(lo, 1e-300))) != np.floor(np.log2(hb))
+        crosses = np.floor(np.log2(np.maximum(lo, 1e-300))) != np.floor(np.log2(np.maximum(hb, 1e-300)))
         assert np.all(crosses[sd != 0]), "a block scale differs away from a power-of-two boundary"
     gv = _dequant(giq, gis)
     unit = np.repeat(np.exp2(gis.astype(np.float64) - 127), 32, axis=-1)
