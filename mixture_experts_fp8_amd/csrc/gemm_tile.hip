@@ -241,30 +241,86 @@ __global__ void __launch_bounds__(64 * (kComputeWaves + kLoaderWaves), 3) tile_k
 #pragma unroll
       for (int c = 0; c < NA; ++c) acc[t][c] = v4f{0.f, 0.f, 0.f, 0.f};
 
-    for (int s = 0; s < KS; ++s) {
-      // this wave's reads of step s - 1 are done; barrier s publishes step s
-      __builtin_amdgcn_s_waitcnt(lgkmcnt_zero());
-      barrier_only();
-      if constexpr (NA > 0) {
-        const uint8_t* base = smem[s % S];
+    if constexpr (NA == 0) {
+      // no columns: only the barriers (0 .. KS - 1)
+      for (int s = 0; s < KS; ++s) barrier_only();
+    } else {
+      // Operands are read from LDS one column group ahead of the MFMAs that
+      // use them, and the next step's weight fragments and first column group
+      // right after the barrier that publishes that step, while the last
+      // column group's MFMAs of the current step still run: the MFMA pipe is
+      // not left idle across the barrier.  Two register sets of weight
+      // fragments (cur / nxt) and two of token fragments (bb[0], bb[1]).
+      struct AOps {
         v4i a[4];
+        uint32_t sa;
+      };
+      v8i bb[2];
+      uint32_t sb[2];
+      auto read_a = [&](AOps& o, int s) {
+        const uint8_t* base = smem[s % S];
 #pragma unroll
         for (int t = 0; t < 4; ++t)
-          a[t] = *reinterpret_cast<const v4i*>(base + G::A + wr * 4096 + t * 1024 + lane * 16);
-        const uint32_t sa = *reinterpret_cast<const uint32_t*>(base + G::AS + wr * 256 + lane * 4);
+          o.a[t] = *reinterpret_cast<const v4i*>(base + G::A + wr * 4096 + t * 1024 + lane * 16);
+        o.sa = *reinterpret_cast<const uint32_t*>(base + G::AS + wr * 256 + lane * 4);
+      };
+      auto read_b = [&](int i, int s, int c) {
+        const uint8_t* base = smem[s % S];
+        const int tok = wc * CGW * 16 + c * 16 + t16;
+        const int sw = (tok >> 1) & 7;
+        const uint8_t* row = base + G::B + tok * 128;
+        bb[i] = join8(*reinterpret_cast<const v4i*>(row + ((g ^ sw) << 4)),
+                      *reinterpret_cast<const v4i*>(row + (((4 + g) ^ sw) << 4)));
+        sb[i] = base[G::BS + tok * 4 + g];
+      };
+      // step s with its weight fragments in cur and its first column group
+      // in bb[P]; when NEXT (s + 1 < KS) also takes barrier s + 1 and reads
+      // step s + 1's into nxt and bb[(P + NA) % 2]
+      auto step = [&](auto p_tag, auto next_tag, int s, AOps& cur, AOps& nxt) {
+        constexpr int P = decltype(p_tag)::value;
+        constexpr bool NEXT = decltype(next_tag)::value;
 #pragma unroll
         for (int c = 0; c < NA; ++c) {
-          const int tok = wc * CGW * 16 + c * 16 + t16;
-          const int sw = (tok >> 1) & 7;
-          const uint8_t* row = base + G::B + tok * 128;
-          const v8i bb = join8(*reinterpret_cast<const v4i*>(row + ((g ^ sw) << 4)),
-                               *reinterpret_cast<const v4i*>(row + (((4 + g) ^ sw) << 4)));
-          const uint32_t sb = (*reinterpret_cast<const uint32_t*>(base + G::BS + tok * 4) >> (8 * g)) & 0xFFu;
-          acc[0][c] = mfma_fp4_fp8<0>(a[0], bb, acc[0][c], sa, sb);
-          acc[1][c] = mfma_fp4_fp8<1>(a[1], bb, acc[1][c], sa, sb);
-          acc[2][c] = mfma_fp4_fp8<2>(a[2], bb, acc[2][c], sa, sb);
-          acc[3][c] = mfma_fp4_fp8<3>(a[3], bb, acc[3][c], sa, sb);
+          const int i = (P + c) % 2;
+          // scheduling fences: the reads are issued before this group's
+          // MFMAs (so they overlap them), and no read moves to another group
+          // (hoisting reads of later groups runs out of registers)
+          __builtin_amdgcn_sched_barrier(0);
+          if (c + 1 < NA) {
+            read_b((P + c + 1) % 2, s, c + 1);
+          } else if (NEXT) {
+            // every read of step s has landed: barrier s + 1 frees its slot
+            // and publishes step s + 1
+            __builtin_amdgcn_s_waitcnt(lgkmcnt_zero());
+            barrier_only();
+            read_a(nxt, s + 1);
+            read_b((P + NA) % 2, s + 1, 0);
+          }
+          __builtin_amdgcn_sched_barrier(0);
+          acc[0][c] = mfma_fp4_fp8<0>(cur.a[0], bb[i], acc[0][c], cur.sa, sb[i]);
+          acc[1][c] = mfma_fp4_fp8<1>(cur.a[1], bb[i], acc[1][c], cur.sa, sb[i]);
+          acc[2][c] = mfma_fp4_fp8<2>(cur.a[2], bb[i], acc[2][c], cur.sa, sb[i]);
+          acc[3][c] = mfma_fp4_fp8<3>(cur.a[3], bb[i], acc[3][c], cur.sa, sb[i]);
         }
+      };
+      using I0 = std::integral_constant<int, 0>;
+      using IQ = std::integral_constant<int, NA % 2>;   // bb index of odd steps' first group
+      using Yes = std::true_type;
+      using No = std::false_type;
+      AOps o0, o1;
+      barrier_only();   // barrier 0 publishes step 0
+      read_a(o0, 0);
+      read_b(0, 0, 0);
+      int s = 0;
+      for (; s + 2 < KS; s += 2) {
+        step(I0{}, Yes{}, s, o0, o1);
+        step(IQ{}, Yes{}, s + 1, o1, o0);
+      }
+      if (s + 1 < KS) {
+        step(I0{}, Yes{}, s, o0, o1);
+        step(IQ{}, No{}, s + 1, o1, o0);
+      } else {
+        step(I0{}, No{}, s, o0, o1);
       }
     }
 
