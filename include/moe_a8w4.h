@@ -22,6 +22,9 @@
  *     y      = w2[e] h                                          (H values)
  *   out[t] = BF16( sum over local k of topk_weights[t,k] * y_(t,k) )
  *   Routes of non-local experts contribute nothing; a token with none gets 0.
+ *   Each term is formed in float32 and held in the route-row format of
+ *   moe_a8w4_stage2 (error at most 2^-14 of the largest magnitude of its
+ *   32-output block) before the float32 sum in ascending k.
  *
  * Conventions
  *   - All data pointers are DEVICE pointers owned by the caller.  The library
@@ -148,19 +151,26 @@ int moe_a8w4_stage1(const moe_a8w4_dims* dims, int32_t block_m, const uint8_t* a
                     const int32_t* num_padded, const uint8_t* w13_p, const uint8_t* w13_s_p,
                     uint8_t* inter_q, uint8_t* inter_s, hipStream_t stream);
 
-/* Stage two: for every local route (t, k), y_routes[t, k, :] (float32,
- * [M, topk, H]) receives topk_weights[t,k] * (w2[e] h), h its dequantised
- * intermediate.  Rows of non-local slots are not written. */
+/* Stage two: for every local route (t, k), row (t, k) of y_routes receives
+ * topk_weights[t,k] * (w2[e] h), h its dequantised intermediate, in the
+ * route-row format: y_routes holds [M, topk, H] int16 codes followed by
+ * [M, topk, H/32] uint8 exponents, M*topk*(2H + H/32) bytes in all (16-byte
+ * aligned).  Each 32 consecutive outputs v of a row share an exponent S =
+ * max(fp32 exponent field of their largest |v|, 14) and are stored as
+ * code = round-to-nearest-even(v * 2^(140 - S)), |code| <= 2^14, read back
+ * exactly as code * 2^(S - 140): an error of at most 2^-14 of the block's
+ * largest magnitude, far finer than a BF16 rounding of each route's share.
+ * Rows of non-local slots are not written. */
 int moe_a8w4_stage2(const moe_a8w4_dims* dims, int32_t block_m, const uint8_t* inter_q,
                     const uint8_t* inter_s, const int32_t* sorted_ids, const int32_t* block_expert,
                     const int32_t* num_padded, const float* topk_weights, const uint8_t* w2_p,
-                    const uint8_t* w2_s_p, float* y_routes, hipStream_t stream);
+                    const uint8_t* w2_s_p, void* y_routes, hipStream_t stream);
 
 /* Top-k combine: out[t, :] (BF16, [M, H]) = round-to-nearest-even of the
- * float32 sum, in ascending k, of y_routes[t, k, :] over the token's local
- * slots (topk_ids decides which slots are local); zero for a token without
- * one.  Bitwise repeatable. */
-int moe_a8w4_combine(const moe_a8w4_dims* dims, const int32_t* topk_ids, const float* y_routes,
+ * float32 sum, in ascending k, of the decoded rows (t, k, :) of y_routes (the
+ * stage-two route rows) over the token's local slots (topk_ids decides which
+ * slots are local); zero for a token without one.  Bitwise repeatable. */
+int moe_a8w4_combine(const moe_a8w4_dims* dims, const int32_t* topk_ids, const void* y_routes,
                      void* out, hipStream_t stream);
 
 /* Name of a status code (static string). */

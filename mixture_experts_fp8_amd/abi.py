@@ -211,11 +211,16 @@ def moe_a8w4_stage1(dims, block_m, a_q, a_s, sorted_ids, block_expert, num_padde
     return inter_q, inter_s
 
 
+def route_rows_bytes(dims):
+    """Bytes of the stage-two route rows: [M, topk, H] int16 codes, then
+    [M, topk, H/32] exponent bytes."""
+    return dims.tokens * dims.topk * (2 * dims.hidden + dims.hidden // 32)
+
+
 def moe_a8w4_stage2(dims, block_m, inter_q, inter_s, sorted_ids, block_expert, num_padded,
                     topk_weights, w2_p, w2_s_p, y_routes=None, stream=None):
     if y_routes is None:
-        y_routes = torch.empty((dims.tokens, dims.topk, dims.hidden), dtype=torch.float32,
-                               device=inter_q.device)
+        y_routes = torch.empty(route_rows_bytes(dims), dtype=torch.uint8, device=inter_q.device)
     st = load().moe_a8w4_stage2(ctypes.byref(dims), block_m, _ptr(inter_q), _ptr(inter_s),
                                 _ptr(sorted_ids), _ptr(block_expert), _ptr(num_padded),
                                 _ptr(topk_weights), _ptr(w2_p), _ptr(w2_s_p), _ptr(y_routes),

@@ -50,6 +50,12 @@ int64_t capacity(const moe_a8w4_dims* d, int bm) {
   return (cap + bm - 1) / bm * bm;
 }
 
+// Route rows: [M, topk, H] 16-bit codes, then [M, topk, H/32] exponent bytes.
+size_t route_codes_bytes(const moe_a8w4_dims* d) { return (size_t)d->tokens * d->topk * d->hidden * 2; }
+size_t route_rows_bytes(const moe_a8w4_dims* d) {
+  return route_codes_bytes(d) + (size_t)d->tokens * d->topk * (d->hidden / 32);
+}
+
 struct Layout {
   size_t aq, as, sorted, bexp, npad, iq, is, y, total;
 };
@@ -68,7 +74,7 @@ Layout layout(const moe_a8w4_dims* d, int bm) {
   L.npad = o;   o += 256;
   L.iq = o;     o += al256(cap * I);
   L.is = o;     o += al256(cap * I / 32);
-  L.y = o;      o += al256(M * (size_t)d->topk * H * 4);
+  L.y = o;      o += al256(route_rows_bytes(d));
   L.total = o;
   return L;
 }
@@ -85,11 +91,13 @@ GemmArgs stage1_args(const moe_a8w4_dims* d, int bm, const uint8_t* a_q, const u
 
 GemmArgs stage2_args(const moe_a8w4_dims* d, int bm, const uint8_t* iq, const uint8_t* is,
                      const int32_t* sorted, const int32_t* bexp, const int32_t* npad,
-                     const float* wts, const uint8_t* w, const uint8_t* ws, float* y) {
+                     const float* wts, const uint8_t* w, const uint8_t* ws, void* y) {
   GemmArgs a = {};
   a.M = d->tokens; a.topk = d->topk; a.N = d->hidden; a.K = d->inter; a.bm = bm;
   a.sorted_ids = sorted; a.block_expert = bexp; a.num_padded = npad;
-  a.bq = iq; a.bs = is; a.w = w; a.ws = ws; a.topk_weights = wts; a.y_routes = y;
+  a.bq = iq; a.bs = is; a.w = w; a.ws = ws; a.topk_weights = wts;
+  a.y_codes = static_cast<int16_t*>(y);
+  a.y_exps = static_cast<uint8_t*>(y) + route_codes_bytes(d);
   return a;
 }
 
@@ -159,7 +167,7 @@ int moe_a8w4_forward(const moe_a8w4_dims* dims, const void* hidden, const int32_
   int32_t* npad = reinterpret_cast<int32_t*>(ws + L.npad);
   uint8_t* iq = ws + L.iq;
   uint8_t* is = ws + L.is;
-  float* y = reinterpret_cast<float*>(ws + L.y);
+  uint8_t* y = ws + L.y;
   const int64_t max_blocks = capacity(dims, bm) / bm;
 
   hipError_t e = moe::launch_prep(topk_ids, dims->tokens, dims->topk, dims->num_experts,
@@ -173,8 +181,8 @@ int moe_a8w4_forward(const moe_a8w4_dims* dims, const void* hidden, const int32_
                                      w2_s_p, y), max_blocks, stream);
   if (e != hipSuccess) return status_of(e);
   return status_of(moe::launch_combine(dims->tokens, dims->hidden, dims->topk, dims->num_experts,
-                                       dims->expert_offset, topk_ids, y,
-                                       static_cast<uint16_t*>(out), stream));
+                                       dims->expert_offset, topk_ids, reinterpret_cast<int16_t*>(y),
+                                       y + route_codes_bytes(dims), static_cast<uint16_t*>(out), stream));
 }
 
 int moe_a8w4_quant_act(int32_t M, int32_t H, const void* x, uint8_t* q, uint8_t* s,
@@ -239,7 +247,7 @@ int moe_a8w4_stage1(const moe_a8w4_dims* dims, int32_t block_m, const uint8_t* a
 int moe_a8w4_stage2(const moe_a8w4_dims* dims, int32_t block_m, const uint8_t* inter_q,
                     const uint8_t* inter_s, const int32_t* sorted_ids, const int32_t* block_expert,
                     const int32_t* num_padded, const float* topk_weights, const uint8_t* w2_p,
-                    const uint8_t* w2_s_p, float* y_routes, hipStream_t stream) {
+                    const uint8_t* w2_s_p, void* y_routes, hipStream_t stream) {
   int st = check_dims(dims);
   if (st) return st;
   if (!valid_bm(block_m)) return MOE_ERR_BLOCK_M;
@@ -257,7 +265,7 @@ int moe_a8w4_stage2(const moe_a8w4_dims* dims, int32_t block_m, const uint8_t* i
                                       max_blocks, stream));
 }
 
-int moe_a8w4_combine(const moe_a8w4_dims* dims, const int32_t* topk_ids, const float* y_routes,
+int moe_a8w4_combine(const moe_a8w4_dims* dims, const int32_t* topk_ids, const void* y_routes,
                      void* out, hipStream_t stream) {
   int st = check_dims(dims);
   if (st) return st;
@@ -265,7 +273,9 @@ int moe_a8w4_combine(const moe_a8w4_dims* dims, const int32_t* topk_ids, const f
   if (!topk_ids || !y_routes || !out) return MOE_ERR_NULL;
   if (!aligned(y_routes, 16) || !aligned(out, 16)) return MOE_ERR_ALIGN;
   return status_of(moe::launch_combine(dims->tokens, dims->hidden, dims->topk, dims->num_experts,
-                                       dims->expert_offset, topk_ids, y_routes,
+                                       dims->expert_offset, topk_ids,
+                                       static_cast<const int16_t*>(y_routes),
+                                       static_cast<const uint8_t*>(y_routes) + route_codes_bytes(dims),
                                        static_cast<uint16_t*>(out), stream));
 }
 

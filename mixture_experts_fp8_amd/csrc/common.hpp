@@ -37,6 +37,22 @@ __device__ __forceinline__ float exp2_neg(int E) {
   return __uint_as_float((uint32_t)(127 - E) << 23);
 }
 
+// Route rows (stage two's per-route outputs, summed by the top-k combine).
+// Each 32 consecutive outputs of a route share an exponent byte S: the fp32
+// exponent field of their largest magnitude, at least 14.  Output v is stored
+// as the 16-bit integer RNE(v * 2^(140 - S)), which lies in [-2^14, 2^14],
+// and decodes exactly to code * 2^(S - 140); the rounding error is at most
+// 2^-14 of the block's largest magnitude (blocks below 2^-112 keep 2^-127
+// absolute).  Finite values only.
+__device__ __forceinline__ int route_block_exp(float amax) {
+  const int ef = (int)((__float_as_uint(amax) >> 23) & 0xFFu);
+  return ef < 14 ? 14 : ef;
+}
+
+// 2^(140 - S) and 2^(S - 140) as fp32 (S in [14, 254]).
+__device__ __forceinline__ float route_encode_mul(int S) { return __uint_as_float((uint32_t)(267 - S) << 23); }
+__device__ __forceinline__ float route_decode_mul(int S) { return __uint_as_float((uint32_t)(S - 13) << 23); }
+
 __device__ __forceinline__ float bf16_to_f32(uint32_t bits16) {
   return __uint_as_float(bits16 << 16);
 }

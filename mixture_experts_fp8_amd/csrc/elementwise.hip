@@ -8,16 +8,18 @@ namespace moe {
 namespace {
 
 // Top-k combine: out[t, h] = BF16( sum over the token's local slots k, in
-// ascending k, of y[t, k, h] ), y already holding topk_weight * (w2 h) of each
-// route in fp32 (the routing weight is applied after stage two: aiter PR
-// 5609, Configuration).  One thread per 8 consecutive outputs; slots whose
-// expert is not local were never written and are skipped, so a token with no
-// local route gets zeros.  The fixed summation order makes the result
-// bitwise repeatable.  H / 8 is a multiple of 64, so the 64 lanes of a wave
-// share one token: its slot mask is uniform, and all of the token's slot
-// loads are issued before the first add.
+// ascending k, of y[t, k, h] ), y holding topk_weight * (w2 h) of each route
+// (the routing weight is applied after stage two: aiter PR 5609,
+// Configuration) in the route-row format: 16-bit codes plus one exponent
+// byte per 32 outputs, decoded exactly to fp32.  One thread per 8
+// consecutive outputs; slots whose expert is not local were never written and
+// are skipped, so a token with no local route gets zeros.  The fixed
+// summation order makes the result bitwise repeatable.  H / 8 is a multiple of
+// 64, so the 64 lanes of a wave share one token: its slot mask is uniform, and
+// all of the token's slot loads are issued before the first add.
 __global__ void __launch_bounds__(256) combine_kernel(const int32_t* __restrict__ ids,
-                                                      const float* __restrict__ y,
+                                                      const int16_t* __restrict__ codes,
+                                                      const uint8_t* __restrict__ exps,
                                                       uint16_t* __restrict__ out, int64_t n8,
                                                       int H, int topk, int E, int expert_offset) {
   const int64_t stride = (int64_t)gridDim.x * blockDim.x;
@@ -29,28 +31,35 @@ __global__ void __launch_bounds__(256) combine_kernel(const int32_t* __restrict_
 #pragma unroll
     for (int k = 0; k < kMaxTopk; ++k)
       if (k < topk && (unsigned)(ids[t * topk + k] - expert_offset) < (unsigned)E) mask |= 1u << k;
-    v4f u[kMaxTopk], v[kMaxTopk];
+    v4i c[kMaxTopk];
+    int sx[kMaxTopk];
 #pragma unroll
     for (int k = 0; k < kMaxTopk; ++k) {
       if (mask & (1u << k)) {
-        const v4f* src = reinterpret_cast<const v4f*>(y + (t * topk + k) * H + h);
-        u[k] = __builtin_nontemporal_load(src);
-        v[k] = __builtin_nontemporal_load(src + 1);
+        const int64_t slot = t * topk + k;
+        c[k] = __builtin_nontemporal_load(reinterpret_cast<const v4i*>(codes + slot * H + h));
+        sx[k] = exps[slot * (H / 32) + h / 32];
       }
     }
-    v4f a = {0.f, 0.f, 0.f, 0.f}, b = a;
+    float a[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int k = 0; k < kMaxTopk; ++k) {
       if (mask & (1u << k)) {
-        a += u[k];
-        b += v[k];
+        const float m = route_decode_mul(sx[k]);
+        const int w[4] = {c[k].x, c[k].y, c[k].z, c[k].w};
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          // code * 2^(S - 140) is exact, so the product rounds nothing
+          a[2 * j] += (float)(int16_t)(w[j] & 0xFFFF) * m;
+          a[2 * j + 1] += (float)(w[j] >> 16) * m;
+        }
       }
     }
     uint4 r;
-    r.x = f32_to_bf16(a.x) | (f32_to_bf16(a.y) << 16);
-    r.y = f32_to_bf16(a.z) | (f32_to_bf16(a.w) << 16);
-    r.z = f32_to_bf16(b.x) | (f32_to_bf16(b.y) << 16);
-    r.w = f32_to_bf16(b.z) | (f32_to_bf16(b.w) << 16);
+    r.x = f32_to_bf16(a[0]) | (f32_to_bf16(a[1]) << 16);
+    r.y = f32_to_bf16(a[2]) | (f32_to_bf16(a[3]) << 16);
+    r.z = f32_to_bf16(a[4]) | (f32_to_bf16(a[5]) << 16);
+    r.w = f32_to_bf16(a[6]) | (f32_to_bf16(a[7]) << 16);
     *reinterpret_cast<uint4*>(out + t * H + h) = r;
   }
 }
@@ -96,11 +105,12 @@ int grid_for(int64_t work, int per_block) {
 }  // namespace
 
 hipError_t launch_combine(int64_t M, int32_t H, int32_t topk, int32_t E, int32_t expert_offset,
-                          const int32_t* ids, const float* y, uint16_t* out, hipStream_t stream) {
+                          const int32_t* ids, const int16_t* y_codes, const uint8_t* y_exps,
+                          uint16_t* out, hipStream_t stream) {
   const int64_t n8 = M * H / 8;
   if (n8 == 0) return hipSuccess;
-  hipLaunchKernelGGL(combine_kernel, dim3(grid_for(n8, 256)), dim3(256), 0, stream, ids, y, out, n8,
-                     H, topk, E, expert_offset);
+  hipLaunchKernelGGL(combine_kernel, dim3(grid_for(n8, 256)), dim3(256), 0, stream, ids, y_codes, y_exps,
+                     out, n8, H, topk, E, expert_offset);
   return hipGetLastError();
 }
 

@@ -76,34 +76,55 @@ __device__ __forceinline__ void wave_lds_sync() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
-// Bytes of wave-private LDS scratch stage2_store needs.
-constexpr int kStage2Scratch = 16 * 272;
+// Bytes of wave-private LDS scratch stage2_store needs: 16 rows of 128 B,
+// padded to 144 so that the 16 rows start in distinct bank groups.
+constexpr int kStage2Scratch = 16 * 144;
 
 // Stage-two epilogue for one 64-row group and one 16-route column group of a
 // wave: lane (t16, g) holds output columns 64 grp + 16g + 4t + r of the route
-// in slot `slot` (negative: no route), wt its routing weight.  The rows
-// wt * value are written to that route's row of y_routes (float32; routes of
-// one token can cancel, and a BF16 rounding of each route's share would then
-// exceed the output tolerance).  They go through the wave's LDS scratch
-// (16 rows of 256 B, padded to 272 against bank conflicts) so that each store
-// instruction writes 4 routes x 256 B in a row instead of 16-byte pieces of 16
-// routes.  All 64 lanes must call it together.
+// in slot `slot` (negative: no route), wt its routing weight.  The values
+// wt * acc go to that route's row in the route-row format (16-bit codes, one
+// exponent byte per 32 columns; the group holds two such blocks, columns
+// 0..31 in lanes g = 0, 1 and 32..63 in g = 2, 3).  The codes go through the
+// wave's LDS scratch so that each store instruction writes 8 routes x 128 B
+// in a row instead of 32-byte pieces of 16 routes.  All 64 lanes must call it
+// together.
 __device__ __forceinline__ void stage2_store(const v4f acc[4], int64_t slot, float wt, const GemmArgs& args,
                                              int grp, int g, uint8_t* scr) {
   const int lane = threadIdx.x & 63, t16 = lane & 15;
+  float v[16];
+  float amax = 0.f;
 #pragma unroll
   for (int t = 0; t < 4; ++t)
-    *reinterpret_cast<v4f*>(scr + t16 * 272 + (16 * g + 4 * t) * 4) =
-        v4f{wt * acc[t][0], wt * acc[t][1], wt * acc[t][2], wt * acc[t][3]};
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      v[4 * t + r] = wt * acc[t][r];
+      amax = fmaxf(amax, fabsf(v[4 * t + r]));
+    }
+  amax = fmaxf(amax, __shfl_xor(amax, 16));
+  const int S = route_block_exp(amax);
+  const float mul = route_encode_mul(S);
+  uint32_t w[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const int c0 = (int)__builtin_rintf(v[2 * j] * mul), c1 = (int)__builtin_rintf(v[2 * j + 1] * mul);
+    w[j] = ((uint32_t)c0 & 0xFFFFu) | ((uint32_t)c1 << 16);
+  }
+  uint8_t* row = scr + t16 * 144 + g * 32;
+  *reinterpret_cast<v4i*>(row) = v4i{(int)w[0], (int)w[1], (int)w[2], (int)w[3]};
+  *reinterpret_cast<v4i*>(row + 16) = v4i{(int)w[4], (int)w[5], (int)w[6], (int)w[7]};
+  const int S1 = __shfl(S, t16 + 32);   // exponent of the second block (lane g = 2)
   wave_lds_sync();
   const int slo = (int)(uint32_t)slot, shi = (int)(slot >> 32);
 #pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    const int route = 4 * q + (lane >> 4), chunk = lane & 15;
+  for (int q = 0; q < 2; ++q) {
+    const int route = 8 * q + (lane >> 3), chunk = lane & 7;
     const int64_t sl = ((int64_t)__shfl(shi, route) << 32) | (uint32_t)__shfl(slo, route);
-    const v4f v = *reinterpret_cast<const v4f*>(scr + route * 272 + chunk * 16);
-    if (sl >= 0) *reinterpret_cast<v4f*>(args.y_routes + sl * args.N + grp * 64 + chunk * 4) = v;
+    const v4i c = *reinterpret_cast<const v4i*>(scr + route * 144 + chunk * 16);
+    if (sl >= 0) *reinterpret_cast<v4i*>(args.y_codes + sl * args.N + grp * 64 + chunk * 8) = c;
   }
+  if (g == 0 && slot >= 0)
+    *reinterpret_cast<uint16_t*>(args.y_exps + slot * (args.N / 32) + 2 * grp) = (uint16_t)(S | (S1 << 8));
   wave_lds_sync();
 }
 

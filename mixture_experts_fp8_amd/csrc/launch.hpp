@@ -23,7 +23,8 @@ struct GemmArgs {
   uint8_t* out_q;         // stage 1: intermediate codes [P, N/2]
   uint8_t* out_s;         // stage 1: intermediate scales [P, N/64]
   const float* topk_weights;  // stage 2: [M, topk]
-  float* y_routes;        // stage 2: weighted route outputs [M, topk, N] fp32
+  int16_t* y_codes;       // stage 2: weighted route outputs [M, topk, N], 16-bit codes
+  uint8_t* y_exps;        //          and their exponent bytes [M, topk, N/32]
 };
 
 // One launch: workgroup 0 sorts the routes (skipped if ids is null), the
@@ -32,7 +33,8 @@ hipError_t launch_prep(const int32_t* ids, int32_t M, int32_t topk, int32_t E, i
                        int32_t bm, int32_t* sorted_ids, int32_t* block_expert, int32_t* num_padded,
                        const uint16_t* x, int64_t H, uint8_t* q, uint8_t* s, hipStream_t stream);
 hipError_t launch_combine(int64_t M, int32_t H, int32_t topk, int32_t E, int32_t expert_offset,
-                          const int32_t* ids, const float* y, uint16_t* out, hipStream_t stream);
+                          const int32_t* ids, const int16_t* y_codes, const uint8_t* y_exps,
+                          uint16_t* out, hipStream_t stream);
 hipError_t launch_pack(const uint8_t* src, const uint8_t* src_s, uint8_t* dst, uint8_t* dst_s,
                        int64_t E, int64_t N, int64_t K, hipStream_t stream);
 // max_blocks: upper bound of sorted blocks (grid size); kernels read the real count on device

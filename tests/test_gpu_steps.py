@@ -7,7 +7,7 @@ import torch
 
 import oracle
 from mixture_experts_fp8_amd import abi, workloads as wl
-from gpu_util import DEV, Layer, check_intermediate, dev, note
+from gpu_util import DEV, Layer, _E4M3, check_intermediate, dev, note
 
 pytestmark = pytest.mark.gpu
 
@@ -175,3 +175,105 @@ def test_stage1_intermediate(name, M, E):
     check_intermediate(L, hidden, ids, routes, giq, gis)
     if w.inter_valid < w.inter:
         assert np.all((giq[:, w.inter_valid:] & 0x7F) == 0)
+
+
+# ------------------------------------------------------------ route rows
+
+_E2M1 = np.array([0, .5, 1, 1.5, 2, 3, 4, 6, -0., -.5, -1, -1.5, -2, -3, -4, -6])
+
+
+def decode_route_rows(buf, M, topk, H):
+    """The stage-two route rows of a uint8 buffer: (codes [M*topk, H] int16,
+    exponents [M*topk, H/32], values [M*topk, H] float64 = code * 2^(S-140))."""
+    nb = M * topk * H * 2
+    codes = buf[:nb].view(np.int16).reshape(M * topk, H)
+    exps = buf[nb:nb + M * topk * H // 32].reshape(M * topk, H // 32)
+    vals = codes.astype(np.float64) * np.repeat(np.exp2(exps.astype(np.float64) - 140), 32, axis=1)
+    return codes, exps, vals
+
+
+def test_combine_route_rows_bit_exact():
+    """Combine of host-written route rows: each output must be the BF16
+    rounding (nearest, ties to even) of the float32 sum, in ascending k, of
+    the exactly decoded values of the token's local slots; zero without one."""
+    w = wl.scaled(wl.WORKLOADS["draft-decode"], num_experts=8, routed_experts=16, expert_offset=4,
+                  config_id=71)
+    M, k, H = 37, 6, 512
+    rng = np.random.default_rng(71)
+    ids = rng.integers(0, 16, size=(M, k)).astype(np.int32)
+    ids[3] = 15                                     # a token with no local slot
+    codes = rng.integers(-16384, 16385, size=(M * k, H)).astype(np.int16)
+    exps = rng.integers(30, 161, size=(M * k, H // 32)).astype(np.uint8)
+    codes[5, :64] = 16384
+    codes[6, :64] = -16384
+    buf = np.concatenate([codes.view(np.uint8).ravel(), exps.ravel()])
+    d = abi.make_dims(M, H, w.inter, w.num_experts, k, w.expert_offset, w.routed_experts)
+    note("combine route rows M=%d k=%d H=%d" % (M, k, H))
+    out = abi.moe_a8w4_combine(d, dev(ids), dev(buf))
+    torch.cuda.synchronize()
+    got = out.view(torch.int16).cpu().numpy().view(np.uint16)
+    vals = (codes.astype(np.float64) * np.repeat(np.exp2(exps.astype(np.float64) - 140), 32, axis=1))
+    vals = vals.astype(np.float32).reshape(M, k, H)   # exact: 15-bit integers times powers of two
+    local = (ids - w.expert_offset >= 0) & (ids - w.expert_offset < w.num_experts)
+    acc = np.zeros((M, H), np.float32)
+    for kk in range(k):
+        acc = np.where(local[:, kk:kk + 1], (acc + vals[:, kk]).astype(np.float32), acc)
+    want = np.array([oracle.bf16_rne(float(x)) for x in acc.ravel()], np.uint16).reshape(M, H)
+    assert np.array_equal(got, want)
+    assert not got[3].any()
+
+
+@pytest.mark.parametrize("name,M,E", [("draft-decode", 33, 8), ("local-slice", 40, 6),
+                                      ("local-slice", 80, 6)])
+def test_stage2_route_rows(name, M, E):
+    """Stage two given the GPU's own intermediate, route by route: decoded rows
+    within the FP32 accumulation budget plus half an encoding step of
+    topk_weight * (w2[e] h) in FP64; exponents as the format defines them
+    (max |code| of a block in [2^13, 2^14] unless the block is tiny); rows of
+    non-local slots untouched."""
+    w = wl.scaled(wl.WORKLOADS[name], num_experts=E, routed_experts=E + 2, config_id=80 + M)
+    L = Layer(w)
+    hidden, ids, wts = wl.make_inputs(w, M, "softmax")
+    d = L.dims(M)
+    bm = abi.moe_a8w4_block_m(d)
+    note("stage2 route rows %s M=%d E=%d bm=%d" % (name, M, E, bm))
+    xd, idd, wd = dev(hidden), dev(ids), dev(wts)
+    q, s = abi.moe_a8w4_quant_act(xd)
+    srt, bexp, npad = abi.moe_a8w4_sort(d, bm, idd)
+    iq, is_ = abi.moe_a8w4_stage1(d, bm, q, s, srt, bexp, npad, L.packed[0], L.packed[1])
+    y = torch.full((abi.route_rows_bytes(d),), 0x5A, dtype=torch.uint8, device=DEV)
+    abi.moe_a8w4_stage2(d, bm, iq, is_, srt, bexp, npad, wd, L.packed[2], L.packed[3], y)
+    torch.cuda.synchronize()
+    H, I, k = w.hidden, w.inter, w.topk
+    codes, exps, got = decode_route_rows(y.cpu().numpy(), M, k, H)
+    P = int(npad.item())
+    sorted_ids = srt[:P].cpu().numpy()
+    giq, gis = iq[:P].cpu().numpy(), is_[:P].cpu().numpy()
+    real = np.nonzero(sorted_ids != M)[0]
+    slots = (sorted_ids[real] & 0xFFFFFF).astype(np.int64) * k + (sorted_ids[real] >> 24)
+    le = ids.ravel()[slots].astype(np.int64) - w.expert_offset
+    h = _E4M3[giq[real]] * np.repeat(np.exp2(gis[real].astype(np.float64) - 127), 32, axis=1)
+    h2, h2s = L.host[2], L.host[3]
+    for e in np.unique(le):
+        rs = np.nonzero(le == e)[0]
+        c = np.empty((H, I), np.uint8)
+        c[:, 0::2] = h2[e] & 15
+        c[:, 1::2] = h2[e] >> 4
+        W = _E2M1[c] * np.repeat(np.exp2(h2s[e].astype(np.float64) - 127), 32, axis=1)
+        wt = wts.ravel()[slots[rs]].astype(np.float64)[:, None]
+        exact = wt * (h[rs] @ W.T)
+        acc_err = 2.0 ** -12 * (I // 128) * np.abs(wt) * np.abs(h[rs]).max(axis=1, keepdims=True) \
+            * np.abs(W).max(axis=1)[None, :]
+        half_step = np.repeat(np.exp2(exps[slots[rs]].astype(np.float64) - 141), 32, axis=1)
+        err = np.abs(got[slots[rs]] - exact)
+        assert np.all(err <= acc_err + half_step), "expert %d: route values off by up to %.3g" % (
+            e, (err - acc_err - half_step).max())
+    blk = np.abs(codes[slots].astype(np.int64)).reshape(len(slots), -1, 32).max(axis=2)
+    ex = exps[slots].astype(np.int64)
+    assert np.all(blk <= 16384) and np.all(ex >= 14) and np.all(ex <= 254)
+    assert np.all(blk[ex > 14] >= 8192), "a block exponent larger than its values need"
+    untouched = np.ones(M * k, bool)
+    untouched[slots] = False
+    raw = y.cpu().numpy()
+    assert np.all(raw[:M * k * H * 2].reshape(M * k, -1)[untouched] == 0x5A)
+    assert np.all(raw[M * k * H * 2:].reshape(M * k, -1)[untouched] == 0x5A)
