@@ -47,8 +47,8 @@ constexpr int kMaxSortBlocks = 64;
 
 struct SortSmem {
   int cnt[kSortWaves][kMaxExperts];                 // per-wave counts, then running offsets
-  int total[kMaxExperts];                           // routes per expert
-  int before[kMaxExperts];                          // of which in earlier chunks
+  int before[kMaxExperts];                          // routes per expert in earlier chunks
+  int after[kMaxExperts];                           // and in later chunks
   int wave_total[kSortWaves];
 };
 
@@ -79,34 +79,58 @@ __device__ void sort_chunk(SortSmem& sm, const int32_t* __restrict__ ids, int M,
 
   for (int i = tid; i < kSortWaves * kMaxExperts; i += kPrepThreads) (&sm.cnt[0][0])[i] = 0;
   for (int i = tid; i < kMaxExperts; i += kPrepThreads) {
-    sm.total[i] = 0;
     sm.before[i] = 0;
+    sm.after[i] = 0;
   }
   __syncthreads();
 
-  // 1. counts over all routes: total, before this chunk, per owning wave
-  constexpr int U = 4;
-  for (int base = 0; base < R; base += U * kPrepThreads) {
-    int le[U];
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int f = base + u * kPrepThreads + tid;
-      le[u] = f < R ? ids[f] - expert_offset : -1;
+  // 1. counts over all routes: before this chunk, per owning wave, after it
+  // (one LDS atomic per route).  Each thread reads 16 B of ids per load and
+  // has the next U loads in flight while it counts the current ones.
+  auto count = [&](int f, int le) {
+    if ((unsigned)le < (unsigned)E) {
+      if (f < g0) atomicAdd(&sm.before[le], 1);
+      else if (f < g1) atomicAdd(&sm.cnt[(f - g0) / C][le], 1);
+      else atomicAdd(&sm.after[le], 1);
     }
+  };
+  constexpr int U = 4;
+  const int R4 = R / 4;   // whole 16-byte groups of ids
+  const int4* ids4 = reinterpret_cast<const int4*>(ids);
+  auto load4 = [&](int4 (&v)[U], int base) {
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      const int f = base + u * kPrepThreads + tid;
-      if ((unsigned)le[u] < (unsigned)E) {
-        atomicAdd(&sm.total[le[u]], 1);
-        if (f < g0) atomicAdd(&sm.before[le[u]], 1);
-        else if (f < g1) atomicAdd(&sm.cnt[(f - g0) / C][le[u]], 1);
+      const int j = base + u * kPrepThreads + tid;
+      v[u] = j < R4 ? ids4[j] : make_int4(-1, -1, -1, -1);
+    }
+  };
+  int4 nxt[U];
+  load4(nxt, 0);
+  for (int base = 0; base < R4; base += U * kPrepThreads) {
+    int4 v[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) v[u] = nxt[u];
+    if (base + U * kPrepThreads < R4) load4(nxt, base + U * kPrepThreads);
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int j = base + u * kPrepThreads + tid;
+      if (j < R4) {
+        count(4 * j, v[u].x - expert_offset);
+        count(4 * j + 1, v[u].y - expert_offset);
+        count(4 * j + 2, v[u].z - expert_offset);
+        count(4 * j + 3, v[u].w - expert_offset);
       }
     }
   }
+  if (tid < R - 4 * R4) count(4 * R4 + tid, ids[4 * R4 + tid] - expert_offset);
   __syncthreads();
 
   // 2. one expert per thread: its count, padded size, and the waves' offsets
-  const int c = tid < E ? sm.total[tid] : 0;
+  int c = 0;
+  if (tid < E) {
+    c = sm.before[tid] + sm.after[tid];
+    for (int j = 0; j < kSortWaves; ++j) c += sm.cnt[j][tid];
+  }
   const int pc = (c + bm - 1) / bm * bm;
   int v = pc;
 #pragma unroll
@@ -141,13 +165,19 @@ __device__ void sort_chunk(SortSmem& sm, const int32_t* __restrict__ ids, int M,
   // 3. each wave places its own routes in order; only wave-private LDS is used
   static_assert(kMaxExperts <= 1023, "expert key needs more bits");
   const unsigned long long below = (1ull << lane) - 1;
-  for (int base = f0; base < f1; base += 64) {
-    const int f = base + lane;
+  auto local_id = [&](int f) {
     int le = -1;
     if (f < f1) {
       le = ids[f] - expert_offset;
       if ((unsigned)le >= (unsigned)E) le = -1;
     }
+    return le;
+  };
+  int le_next = local_id(f0 + lane);   // one piece of 64 ahead
+  for (int base = f0; base < f1; base += 64) {
+    const int f = base + lane;
+    const int le = le_next;
+    le_next = local_id(base + 64 + lane);
     const int key = le + 1;   // 0 for no local route
     unsigned long long same = ~0ull;
 #pragma unroll
