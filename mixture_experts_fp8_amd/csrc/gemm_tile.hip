@@ -26,10 +26,11 @@
 //                                               lanes of one operand read hit 16
 //                                               distinct 16-byte bank slots
 //   As  [4 row groups][64 lanes][4]             E8M0 weight scales
-//   Bs  [4 copies][64 tokens][4]                E8M0 token scales; loader l
-//                                               loads tokens 64 (l mod BM/64) +
-//                                               lane, so tokens 0..BM-1 sit in
-//                                               order at the start of the area
+//   Bs  [BM tokens][4]                          E8M0 token scales; loader
+//                                               l < BM/64 loads tokens 64 l +
+//                                               lane (one 4-byte gather from 64
+//                                               token rows, so no other loader
+//                                               repeats it)
 //
 // Barrier s: every loader has waited until its loads of step s have landed
 // (vmcnt), every compute wave until its LDS reads of step s - 1 are done.  It
@@ -88,7 +89,8 @@ struct TileGeom {
   static constexpr int AS = B + BM * 128;
   static constexpr int BS = AS + 1024;
   static constexpr int BYTES = BS + 1024;
-  static constexpr int LOADS = 4 + NBCH + 2;        // per loader and step: A, B chunks, As, Bs
+  static constexpr int NBS = BM / 64;               // loaders that also load token scales
+  static constexpr int LOADS = 4 + NBCH + 1;        // per loader and step: A, B chunks, As (+ Bs)
 };
 
 // s_waitcnt immediates (gfx9 encoding): wait on the vector-memory counter
@@ -186,7 +188,8 @@ __global__ void __launch_bounds__(64 * (kComputeWaves + kLoaderWaves), 3) tile_k
       const int piece = (lane & 7) ^ ((t >> 1) & 7);
       gB[i] = args.bq + brow(t) * K + piece * 16;
     }
-    constexpr int NBS = BM / 64;
+    constexpr int NBS = G::NBS;
+    const bool has_bs = l < NBS;   // loader l < NBS brings the scales of tokens [64 l, +64)
     const uint8_t* gBs = args.bs + brow((l % NBS) * 64 + lane) * (K / 32);
     const uint32_t lds0 = lds_addr(&smem[0][0]);
     auto issue = [&](int s) {
@@ -197,7 +200,7 @@ __global__ void __launch_bounds__(64 * (kComputeWaves + kLoaderWaves), 3) tile_k
 #pragma unroll
       for (int i = 0; i < G::NBCH; ++i) dma16_b(gB[i] + s * 128, base + G::B + (l * G::NBCH + i) * 1024);
       dma4(gAs + (int64_t)s * 256, base + G::AS + l * 256);
-      dma4(gBs + 4 * s, base + G::BS + l * 256);
+      if (has_bs) dma4(gBs + 4 * s, base + G::BS + l * 256);
     };
 #pragma unroll
     for (int s = 0; s < S - 1; ++s)
@@ -205,8 +208,12 @@ __global__ void __launch_bounds__(64 * (kComputeWaves + kLoaderWaves), 3) tile_k
     for (int s = 0; s < KS; ++s) {
       // barrier s publishes step s: it has landed once at most the loads of
       // steps s+1 .. s+S-2 are outstanding (near the end: none)
-      if (s + S - 2 < KS) __builtin_amdgcn_s_waitcnt(vmcnt_only((S - 2) * G::LOADS));
-      else __builtin_amdgcn_s_waitcnt(vmcnt_only(0));
+      if (s + S - 2 < KS) {
+        if (has_bs) __builtin_amdgcn_s_waitcnt(vmcnt_only((S - 2) * (G::LOADS + 1)));
+        else __builtin_amdgcn_s_waitcnt(vmcnt_only((S - 2) * G::LOADS));
+      } else {
+        __builtin_amdgcn_s_waitcnt(vmcnt_only(0));
+      }
       barrier_only();
       // every compute wave has finished reading step s - 1: refill its slot
       if (s + S - 1 < KS) issue(s + S - 1);
