@@ -26,11 +26,15 @@
 //                                               lanes of one operand read hit 16
 //                                               distinct 16-byte bank slots
 //   As  [4 row groups][64 lanes][4]             E8M0 weight scales
-//   Bs  [BM tokens][4]                          E8M0 token scales; loader
-//                                               l < BM/64 loads tokens 64 l +
-//                                               lane (one 4-byte gather from 64
-//                                               token rows, so no other loader
-//                                               repeats it)
+//   Bs  [BM tokens][4]                          E8M0 token scales, used only
+//                                               when the tile's scales do not
+//                                               fit the preload area below;
+//                                               loader l < BM/64 loads tokens
+//                                               64 l + lane
+//
+// Token scales otherwise: all BM x K/32 of the tile in a separate LDS area,
+// token-major, loaded before step 0 (one short row per token instead of a
+// 4-byte gather from every token row at every step).
 //
 // Barrier s: every loader has waited until its loads of step s have landed
 // (vmcnt), every compute wave until its LDS reads of step s - 1 are done.  It
@@ -144,12 +148,20 @@ __device__ __forceinline__ void expert_major(int t, int NT, int nblk, const int3
 }
 
 constexpr int kComputeWaves = 8, kLoaderWaves = 4;
+// LDS for a tile's token scales, loaded once at the tile's start (a gather of
+// one short row per token) instead of one 4-byte gather per token and step:
+// up to block_m x K / 32 bytes (K <= 8192 at block_m 128), so that a loader
+// issues at most 32 such loads.
+constexpr int kScalePreloadBytes = 32 * 1024;
 
-template <int STAGE, int CGW, int S>
+// PRE: the tile's token scales are preloaded (BM x K/32 <= kScalePreloadBytes).
+template <int STAGE, int CGW, int S, bool PRE>
 __global__ void __launch_bounds__(64 * (kComputeWaves + kLoaderWaves), 3) tile_kernel(GemmArgs args) {
   using G = TileGeom<CGW>;
   constexpr int BM = G::BM;
   __shared__ __attribute__((aligned(1024))) uint8_t smem[S][G::BYTES];
+  // all token scales of the tile, [BM tokens][K / 32], when they fit
+  __shared__ __attribute__((aligned(16))) uint8_t spre[PRE ? kScalePreloadBytes : 16];
 
   const int N = args.N, K = args.K, M = args.M;
   const int KS = K / 128;
@@ -189,9 +201,28 @@ __global__ void __launch_bounds__(64 * (kComputeWaves + kLoaderWaves), 3) tile_k
       gB[i] = args.bq + brow(t) * K + piece * 16;
     }
     constexpr int NBS = G::NBS;
-    const bool has_bs = l < NBS;   // loader l < NBS brings the scales of tokens [64 l, +64)
+    // per-step token scales (only without the preload): loader l < NBS
+    // brings those of tokens [64 l, +64)
+    const bool has_bs = !PRE && l < NBS;
     const uint8_t* gBs = args.bs + brow((l % NBS) * 64 + lane) * (K / 32);
     const uint32_t lds0 = lds_addr(&smem[0][0]);
+    if constexpr (PRE) {
+      // the tile's token scales as one flat run of BM * KS words (word d:
+      // token d / KS, step d % KS), 64 words per load, the loaders taking
+      // turns; issued before step 0, so barrier 0 also covers them
+      const uint32_t pre0 = lds_addr(&spre[0]);
+      // the rows of tokens lane and 64 + lane, fetched once; each load then
+      // takes its tokens' rows from the lanes that hold them
+      const int row_lo = (int)brow(lane);
+      const int row_hi = BM > 64 ? (int)brow(64 + lane) : 0;
+      for (int d0 = l * 64; d0 < BM * KS; d0 += kLoaderWaves * 64) {
+        const int d = d0 + lane;
+        const int u = d / KS;
+        const int r_lo = __shfl(row_lo, u & 63), r_hi = __shfl(row_hi, u & 63);
+        const int64_t row = u < 64 ? r_lo : r_hi;
+        dma4(args.bs + row * (K / 32) + 4 * (d - u * KS), pre0 + (uint32_t)d0 * 4);
+      }
+    }
     auto issue = [&](int s) {
       const uint32_t base = lds0 + (uint32_t)(s % S) * G::BYTES;
 #pragma unroll
@@ -278,7 +309,7 @@ __global__ void __launch_bounds__(64 * (kComputeWaves + kLoaderWaves), 3) tile_k
         const uint8_t* row = base + G::B + tok * 128;
         bb[i] = join8(*reinterpret_cast<const v4i*>(row + ((g ^ sw) << 4)),
                       *reinterpret_cast<const v4i*>(row + (((4 + g) ^ sw) << 4)));
-        sb[i] = base[G::BS + tok * 4 + g];
+        sb[i] = PRE ? spre[(tok * KS + s) * 4 + g] : base[G::BS + tok * 4 + g];
       };
       // step s with its weight fragments in cur and its first column group
       // in bb[P]; when NEXT (s + 1 < KS) also takes barrier s + 1 and reads
@@ -371,6 +402,17 @@ __global__ void __launch_bounds__(64 * (kComputeWaves + kLoaderWaves), 3) tile_k
 #endif
 static_assert(MOE_TILE_STAGES >= 3, "the stage-two epilogue borrows the two ring slots not read last");
 
+// The preload pays at block_m 64 (stage one at local-slice M=4096: -6 %); at
+// block_m 128 its wait before step 0 costs more than the per-step gathers it
+// saves (+4 % at M=16384), so those tiles keep the per-step loads.
+template <int STAGE, int CGW, int S>
+void launch_one(const GemmArgs& a, dim3 g, dim3 blk, hipStream_t stream) {
+  if (CGW == 2 && 32 * CGW * (a.K / 128) * 4 <= kScalePreloadBytes)
+    hipLaunchKernelGGL((tile_kernel<STAGE, CGW, S, true>), g, blk, 0, stream, a);
+  else
+    hipLaunchKernelGGL((tile_kernel<STAGE, CGW, S, false>), g, blk, 0, stream, a);
+}
+
 }  // namespace
 
 hipError_t launch_tile(int stage, const GemmArgs& a, int64_t max_blocks, hipStream_t stream) {
@@ -378,10 +420,10 @@ hipError_t launch_tile(int stage, const GemmArgs& a, int64_t max_blocks, hipStre
   const int64_t grid = max_blocks * (a.N / 256);
   if (grid <= 0) return hipSuccess;
   const dim3 g((unsigned)grid), blk(64 * (kComputeWaves + kLoaderWaves));
-  if (stage == 1 && a.bm == 128) hipLaunchKernelGGL((tile_kernel<1, 4, S>), g, blk, 0, stream, a);
-  else if (stage == 1 && a.bm == 64) hipLaunchKernelGGL((tile_kernel<1, 2, S>), g, blk, 0, stream, a);
-  else if (stage == 2 && a.bm == 128) hipLaunchKernelGGL((tile_kernel<2, 4, S>), g, blk, 0, stream, a);
-  else if (stage == 2 && a.bm == 64) hipLaunchKernelGGL((tile_kernel<2, 2, S>), g, blk, 0, stream, a);
+  if (stage == 1 && a.bm == 128) launch_one<1, 4, S>(a, g, blk, stream);
+  else if (stage == 1 && a.bm == 64) launch_one<1, 2, S>(a, g, blk, stream);
+  else if (stage == 2 && a.bm == 128) launch_one<2, 4, S>(a, g, blk, stream);
+  else if (stage == 2 && a.bm == 64) launch_one<2, 2, S>(a, g, blk, stream);
   else return hipErrorInvalidValue;
   return hipGetLastError();
 }
