@@ -39,7 +39,7 @@ int choose_bm(const moe_a8w4_dims* d) {
   const double avg = (double)d->tokens * d->topk / experts;
   if (avg <= 8.0) return 16;
   if (avg <= 24.0) return 32;
-  if (avg <= 64.0) return 64;
+  if (avg <= 40.0) return 64;
   return 128;
 }
 

@@ -85,7 +85,9 @@ def test_block_m_capacity_and_workspace_sizes():
     assert abi.moe_a8w4_block_m(dims(tokens=16384, num_experts=96, topk=6, inter=2304)) == 128
     # a 96-expert slice of a 384-expert router: 1024 tokens give 16 routes per expert
     d = dims(tokens=1024, num_experts=96, topk=6, inter=2304)
-    assert abi.moe_a8w4_block_m(d) == 64          # as if all 6 slots were local
+    assert abi.moe_a8w4_block_m(d) == 128         # as if all 6 slots were local (64 per expert)
+    assert abi.moe_a8w4_block_m(dims(tokens=640, num_experts=96, topk=6)) == 64    # 40 per expert
+    assert abi.moe_a8w4_block_m(dims(tokens=656, num_experts=96, topk=6)) == 128   # 41
     d.routed_experts = 384
     assert abi.moe_a8w4_block_m(d) == 32
     d.routed_experts = -1

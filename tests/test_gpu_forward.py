@@ -96,9 +96,9 @@ def test_forward_full_size_sampled(layers, name, M, mode):
 TILE_SHAPES = [  # (hidden, inter, experts, topk, tokens): block_m 64/128 with short and odd K
     (512, 128, 4, 2, 300),    # stage two has a single K step
     (1024, 384, 3, 1, 200),   # stage two has three K steps (ring of three)
-    (512, 256, 8, 2, 200),    # block_m 64, two K steps in stage two
+    (512, 256, 8, 2, 150),    # block_m 64, two K steps in stage two
     (8704, 256, 2, 1, 300),   # block_m 128, long K (68 steps in stage one)
-    (16896, 128, 4, 1, 200),  # block_m 64, token scales too many to preload (K > 16384)
+    (16896, 128, 4, 1, 150),  # block_m 64, token scales too many to preload (K > 16384)
 ]
 
 
