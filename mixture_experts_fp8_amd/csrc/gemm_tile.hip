@@ -397,6 +397,190 @@ __global__ void __launch_bounds__(64 * (kComputeWaves + kLoaderWaves), 3) tile_k
   }
 }
 
+// ------------------------------------------------ short K: tokens resident
+//
+// For a short reduction (K <= kResidentBytes / BM, e.g. stage two at I 640)
+// a 256-row tile has only a few K steps, so the pipeline fill and the
+// epilogue dominate and every slice re-reads the block's tokens.  Here a
+// workgroup keeps the block's whole token tile (BM x K codes and their
+// scales) in LDS, loaded once, and runs NS consecutive 256-row weight slices
+// against it: NS x KS steps in which only the weights stream through the
+// ring, an epilogue after every KS of them.  Same waves and per-step MFMAs as
+// tile_kernel; the loaders run on into the next slice while the compute
+// waves store the previous one.
+constexpr int kResidentBytes = 80 * 1024;
+
+template <int STAGE, int CGW, int S, int NS>
+__global__ void __launch_bounds__(64 * (kComputeWaves + kLoaderWaves), 3) tile_resident_kernel(GemmArgs args) {
+  constexpr int BM = 32 * CGW;
+  constexpr int NBCH = CGW;                 // 1 KB token chunks per loader and K step
+  constexpr int SLOT = 16384 + 1024;        // ring slot: A [4][4][64][16], As [4][64][4]
+  constexpr int LOADS = 4 + 1;              // per loader and step
+  __shared__ __attribute__((aligned(1024))) uint8_t ring[S][SLOT];
+  // token codes, step-major: step s at s * BM * 128, laid out as tile_kernel's B
+  __shared__ __attribute__((aligned(1024))) uint8_t sB[kResidentBytes];
+  // token scales, token-major [BM][K / 32]
+  __shared__ __attribute__((aligned(16))) uint8_t sBs[kResidentBytes / 32];
+  // stage two: wave-private scratch of the route-row stores (the ring holds
+  // the next slice's steps while a slice is stored)
+  __shared__ __attribute__((aligned(16))) uint8_t scr_all[STAGE == 2 ? kComputeWaves : 1]
+                                                        [STAGE == 2 ? kStage2Scratch : 16];
+
+  const int N = args.N, K = args.K, M = args.M;
+  const int KS = K / 128;
+  const int NG = N / (256 * NS);            // slice groups per block
+  const int nblk = *args.num_padded / BM;
+  const int T = nblk * NG;
+  if ((int)blockIdx.x >= T) return;
+  int b, sg;
+  expert_major(xcd_tile(blockIdx.x, T), NG, nblk, args.block_expert, b, sg);
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int32_t* ids = args.sorted_ids + (int64_t)b * BM;
+  const int Q = NS * KS;                    // steps of the tile: slice q / KS, K step q % KS
+
+  if (wave >= kComputeWaves) {
+    // ------------------------------------------------------------ loader
+    const int l = wave - kComputeWaves;
+    const int e = args.block_expert[b];
+    const int first = ids[0];
+    auto brow = [&](int t) -> int64_t {
+      if (STAGE == 1) {
+        const int r = ids[t];
+        return (int64_t)((r == M ? first : r) & 0xFFFFFF);
+      }
+      return (int64_t)b * BM + t;
+    };
+    // the resident token tile: loader l brings chunks l NBCH .. of every step
+#pragma unroll
+    for (int i = 0; i < NBCH; ++i) {
+      const int t = 8 * (l * NBCH + i) + (lane >> 3);
+      const int piece = (lane & 7) ^ ((t >> 1) & 7);
+      const uint8_t* src = args.bq + brow(t) * K + piece * 16;
+      const uint32_t dst = lds_addr(&sB[0]) + (uint32_t)(l * NBCH + i) * 1024;
+      for (int ks = 0; ks < KS; ++ks) dma16_b(src + ks * 128, dst + (uint32_t)ks * BM * 128);
+    }
+    {
+      // token scales as one flat run of BM * KS words (word d: token d / KS,
+      // step d % KS), each load taking its tokens' rows from the lanes that
+      // hold them
+      const int row_lo = (int)brow(lane);
+      const int row_hi = BM > 64 ? (int)brow(64 + lane) : 0;
+      const uint32_t s0 = lds_addr(&sBs[0]);
+      for (int d0 = l * 64; d0 < BM * KS; d0 += kLoaderWaves * 64) {
+        const int d = d0 + lane;
+        const int u = d / KS;
+        const int r_lo = __shfl(row_lo, u & 63), r_hi = __shfl(row_hi, u & 63);
+        const int64_t row = u < 64 ? r_lo : r_hi;
+        dma4(args.bs + row * (K / 32) + 4 * (d - u * KS), s0 + (uint32_t)d0 * 4);
+      }
+    }
+    // weights: slice j of the group is row groups (sg NS + j) 4 + l of expert e
+    const uint8_t* gA = args.w + (int64_t)e * ((int64_t)N * K / 2) + (int64_t)(sg * NS * 4 + l) * KS * 4096 +
+                        lane * 16;
+    const uint8_t* gAs = args.ws + (int64_t)e * ((int64_t)N * K / 32) + (int64_t)(sg * NS * 4 + l) * KS * 256 +
+                         lane * 4;
+    const uint32_t lds0 = lds_addr(&ring[0][0]);
+    auto issue = [&](int q) {
+      const int j = q / KS, ks = q - j * KS;
+      const int64_t step = (int64_t)j * 4 * KS + ks;   // row group advances by 4 per slice
+      const uint32_t base = lds0 + (uint32_t)(q % S) * SLOT;
+#pragma unroll
+      for (int t = 0; t < 4; ++t) dma16_a(gA + step * 4096 + t * 1024, base + l * 4096 + t * 1024);
+      dma4(gAs + step * 256, base + 16384 + l * 256);
+    };
+#pragma unroll
+    for (int q = 0; q < S - 1; ++q)
+      if (q < Q) issue(q);
+    for (int q = 0; q < Q; ++q) {
+      // barrier q publishes step q (and, at q = 0, the resident tile issued
+      // before it)
+      if (q + S - 2 < Q) __builtin_amdgcn_s_waitcnt(vmcnt_only((S - 2) * LOADS));
+      else __builtin_amdgcn_s_waitcnt(vmcnt_only(0));
+      barrier_only();
+      if (q + S - 1 < Q) issue(q + S - 1);
+    }
+    return;
+  }
+
+  // -------------------------------------------------------------- compute
+  const int wr = wave >> 1, wc = wave & 1;
+  const int t16 = lane & 15, g = lane >> 4;
+  uint8_t* scr = &scr_all[STAGE == 2 ? wave : 0][0];
+
+  auto run = [&](auto na_tag) {
+    constexpr int NA = decltype(na_tag)::value;
+    int64_t slot[NA > 0 ? NA : 1];
+    float wt[NA > 0 ? NA : 1];
+    if constexpr (STAGE == 2) {
+#pragma unroll
+      for (int c = 0; c < NA; ++c) {
+        const int rid = ids[wc * CGW * 16 + c * 16 + t16];
+        slot[c] = rid == M ? -1 : route_slot(rid, args.topk);
+        wt[c] = rid == M ? 0.f : args.topk_weights[slot[c]];
+      }
+    }
+    for (int j = 0; j < NS; ++j) {
+      v4f acc[4][NA > 0 ? NA : 1];
+#pragma unroll
+      for (int t = 0; t < 4; ++t)
+#pragma unroll
+        for (int c = 0; c < NA; ++c) acc[t][c] = v4f{0.f, 0.f, 0.f, 0.f};
+      for (int ks = 0; ks < KS; ++ks) {
+        const int q = j * KS + ks;
+        __builtin_amdgcn_s_waitcnt(lgkmcnt_zero());
+        barrier_only();
+        if constexpr (NA > 0) {
+          const uint8_t* base = ring[q % S];
+          v4i a[4];
+#pragma unroll
+          for (int t = 0; t < 4; ++t)
+            a[t] = *reinterpret_cast<const v4i*>(base + wr * 4096 + t * 1024 + lane * 16);
+          const uint32_t sa = *reinterpret_cast<const uint32_t*>(base + 16384 + wr * 256 + lane * 4);
+          const uint8_t* bstep = sB + ks * BM * 128;
+#pragma unroll
+          for (int c = 0; c < NA; ++c) {
+            const int tok = wc * CGW * 16 + c * 16 + t16;
+            const int sw = (tok >> 1) & 7;
+            const uint8_t* row = bstep + tok * 128;
+            const v8i bb = join8(*reinterpret_cast<const v4i*>(row + ((g ^ sw) << 4)),
+                                 *reinterpret_cast<const v4i*>(row + (((4 + g) ^ sw) << 4)));
+            const uint32_t sb = sBs[(tok * KS + ks) * 4 + g];
+            acc[0][c] = mfma_fp4_fp8<0>(a[0], bb, acc[0][c], sa, sb);
+            acc[1][c] = mfma_fp4_fp8<1>(a[1], bb, acc[1][c], sa, sb);
+            acc[2][c] = mfma_fp4_fp8<2>(a[2], bb, acc[2][c], sa, sb);
+            acc[3][c] = mfma_fp4_fp8<3>(a[3], bb, acc[3][c], sa, sb);
+          }
+        }
+      }
+      const int grp = (sg * NS + j) * 4 + wr;
+#pragma unroll
+      for (int c = 0; c < NA; ++c) {
+        const v4f part[4] = {acc[0][c], acc[1][c], acc[2][c], acc[3][c]};
+        if constexpr (STAGE == 1) {
+          const int col = wc * CGW * 16 + c * 16 + t16;
+          stage1_store(part, (int64_t)b * BM + col, grp, N / 2, g, args.out_q, args.out_s);
+        } else {
+          stage2_store(part, slot[c], wt[c], args, grp, g, scr);
+        }
+      }
+    }
+  };
+
+  int nact = 0;
+#pragma unroll
+  for (int c = 0; c < CGW; ++c)
+    if (__ballot(ids[wc * CGW * 16 + c * 16 + t16] != M) != 0) nact = c + 1;
+  nact = __builtin_amdgcn_readfirstlane(nact);
+  if (nact == CGW) run(std::integral_constant<int, CGW>{});
+  else if (nact == 0) run(std::integral_constant<int, 0>{});
+  else if (nact == 1) run(std::integral_constant<int, 1>{});
+  else if constexpr (CGW > 2) {
+    if (nact == 2) run(std::integral_constant<int, 2>{});
+    else run(std::integral_constant<int, 3>{});
+  }
+}
+
 #ifndef MOE_TILE_STAGES
 #define MOE_TILE_STAGES 3
 #endif
@@ -405,8 +589,26 @@ static_assert(MOE_TILE_STAGES >= 3, "the stage-two epilogue borrows the two ring
 // The preload pays at block_m 64 (stage one at local-slice M=4096: -6 %); at
 // block_m 128 its wait before step 0 costs more than the per-step gathers it
 // saves (+4 % at M=16384), so those tiles keep the per-step loads.
+// Slices per workgroup of the token-resident kernel for this launch (0: not
+// used): the token tile must fit, and the 256-row slices split into groups
+// of 4 or 5.
+int resident_slices(const GemmArgs& a) {
+  if ((int64_t)a.bm * a.K > kResidentBytes) return 0;
+  const int slices = a.N / 256;
+  if (slices % 4 == 0) return 4;
+  if (slices % 5 == 0) return 5;
+  return 0;
+}
+
 template <int STAGE, int CGW, int S>
 void launch_one(const GemmArgs& a, dim3 g, dim3 blk, hipStream_t stream) {
+  const int ns = resident_slices(a);
+  if (ns == 4 || ns == 5) {
+    const dim3 gr((unsigned)(g.x / ns));
+    if (ns == 4) hipLaunchKernelGGL((tile_resident_kernel<STAGE, CGW, S, 4>), gr, blk, 0, stream, a);
+    else hipLaunchKernelGGL((tile_resident_kernel<STAGE, CGW, S, 5>), gr, blk, 0, stream, a);
+    return;
+  }
   if (CGW == 2 && 32 * CGW * (a.K / 128) * 4 <= kScalePreloadBytes)
     hipLaunchKernelGGL((tile_kernel<STAGE, CGW, S, true>), g, blk, 0, stream, a);
   else

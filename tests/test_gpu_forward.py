@@ -99,6 +99,10 @@ TILE_SHAPES = [  # (hidden, inter, experts, topk, tokens): block_m 64/128 with s
     (512, 256, 8, 2, 150),    # block_m 64, two K steps in stage two
     (8704, 256, 2, 1, 300),   # block_m 128, long K (68 steps in stage one)
     (16896, 128, 4, 1, 150),  # block_m 64, token scales too many to preload (K > 16384)
+    # token-resident kernel (the block's tokens stay in LDS, 4 or 5 weight slices per workgroup)
+    (1024, 640, 4, 2, 150),   # block_m 128, stage two resident at the size limit (128 x 640)
+    (1024, 512, 4, 2, 70),    # block_m 64, both stages resident, 4 slices
+    (512, 640, 4, 2, 150),    # block_m 128, stage one resident with 5 slices (N = 1280)
 ]
 
 
