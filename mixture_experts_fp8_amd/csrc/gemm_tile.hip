@@ -586,28 +586,36 @@ __global__ void __launch_bounds__(64 * (kComputeWaves + kLoaderWaves), 3) tile_r
 #endif
 static_assert(MOE_TILE_STAGES >= 3, "the stage-two epilogue borrows the two ring slots not read last");
 
-// The preload pays at block_m 64 (stage one at local-slice M=4096: -6 %); at
-// block_m 128 its wait before step 0 costs more than the per-step gathers it
-// saves (+4 % at M=16384), so those tiles keep the per-step loads.
 // Slices per workgroup of the token-resident kernel for this launch (0: not
-// used): the token tile must fit, and the 256-row slices split into groups
-// of 4 or 5.
-int resident_slices(const GemmArgs& a) {
+// used): the token tile must fit; of the group sizes that split the 256-row
+// slices evenly, the largest that still leaves two workgroups per CU (at
+// prefill-shared M=16384 stage two: 4 slices 749 us, 10 slices 690 us, 20
+// slices 762 us, too few workgroups), else the smallest.
+int resident_slices(const GemmArgs& a, int64_t max_tiles) {
   if ((int64_t)a.bm * a.K > kResidentBytes) return 0;
   const int slices = a.N / 256;
-  if (slices % 4 == 0) return 4;
-  if (slices % 5 == 0) return 5;
-  return 0;
+  int pick = 0;
+  for (int ns : {4, 5, 10}) {
+    if (slices % ns) continue;
+    if (pick == 0 || max_tiles / ns >= 512) pick = ns;
+  }
+  return pick;
 }
 
+// Token-resident kernel where resident_slices allows, else tile_kernel. Its
+// scale preload pays at block_m 64 (stage one at local-slice M=4096: -6 %); at
+// block_m 128 the wait before step 0 costs more than the per-step gathers it
+// saves (+4 % at M=16384), so those tiles keep the per-step loads.
 template <int STAGE, int CGW, int S>
 void launch_one(const GemmArgs& a, dim3 g, dim3 blk, hipStream_t stream) {
-  const int ns = resident_slices(a);
-  if (ns == 4 || ns == 5) {
+  const int ns = resident_slices(a, g.x);
+  if (ns > 0) {
     const dim3 gr((unsigned)(g.x / ns));
-    if (ns == 4) hipLaunchKernelGGL((tile_resident_kernel<STAGE, CGW, S, 4>), gr, blk, 0, stream, a);
-    else hipLaunchKernelGGL((tile_resident_kernel<STAGE, CGW, S, 5>), gr, blk, 0, stream, a);
-    return;
+    switch (ns) {
+      case 4: hipLaunchKernelGGL((tile_resident_kernel<STAGE, CGW, S, 4>), gr, blk, 0, stream, a); return;
+      case 5: hipLaunchKernelGGL((tile_resident_kernel<STAGE, CGW, S, 5>), gr, blk, 0, stream, a); return;
+      default: hipLaunchKernelGGL((tile_resident_kernel<STAGE, CGW, S, 10>), gr, blk, 0, stream, a); return;
+    }
   }
   if (CGW == 2 && 32 * CGW * (a.K / 128) * 4 <= kScalePreloadBytes)
     hipLaunchKernelGGL((tile_kernel<STAGE, CGW, S, true>), g, blk, 0, stream, a);
