@@ -81,6 +81,8 @@ def _load():
     lib.oracle_forward_given_intermediate.argtypes = ([c_i64, c_i64, c_i64, c_int, c_int, c_int]
                                                       + [vp] * 4 + [vp, c_i64, vp, vp, vp, vp])
     lib.oracle_forward_given_intermediate.restype = None
+    lib.oracle_softmax_topk.argtypes = [c_i64, c_int, c_int, c_int, vp, vp, vp]
+    lib.oracle_softmax_topk.restype = None
     lib.oracle_num_threads.argtypes = []
     lib.oracle_num_threads.restype = c_int
     _lib = lib
@@ -261,6 +263,21 @@ def forward_given_intermediate(topk_ids, topk_weights, w2, w2_s, inter_q, inter_
                                               _p(w2), _p(w2_s), _p(tok), ntok, _p(iq), _p(is_),
                                               _p(o64), _p(out))
     return (out, o64) if want_f64 else out
+
+
+def softmax_topk(logits, k_routed: int, shared_id: int = -1):
+    """Router: (ids int32 [M, k], weights float64 [M, k]) for logits float32
+    [M, E_routed]: the k_routed largest logits (lower id on ties) in
+    descending order, weighted by the softmax of the chosen logits; with
+    shared_id >= 0 a last slot holding that expert with weight 1."""
+    lg = _c(logits, np.float32)
+    M, Er = lg.shape
+    assert 1 <= k_routed <= Er
+    k = k_routed + (1 if shared_id >= 0 else 0)
+    ids = np.zeros((M, k), np.int32)
+    wts = np.zeros((M, k), np.float64)
+    _load().oracle_softmax_topk(M, Er, k_routed, shared_id, _p(lg), _p(ids), _p(wts))
+    return ids, wts
 
 
 def num_threads() -> int:

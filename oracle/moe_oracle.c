@@ -440,6 +440,46 @@ void oracle_intermediate(int64_t M, int64_t H, int64_t I, int E, int expert_offs
     }
 }
 
+/* Router of the backbone configurations: for each token, its k_routed
+ * largest logits among E_routed (equal values: the lower expert id first),
+ * in descending order, and as weights the softmax of the chosen logits --
+ * the softmax over all E_routed logits renormalised over the chosen ones,
+ * which is the same in exact arithmetic -- in FP64.  With a shared expert
+ * (shared_id >= 0), slot k_routed holds it with weight 1 (the "fused shared
+ * expert" of the prefill configuration).  logits [M, E_routed] float32;
+ * ids [M, k] int32 and weights [M, k] double, k = k_routed + (shared >= 0). */
+void oracle_softmax_topk(int64_t M, int Er, int kr, int shared_id, const float* logits,
+                         int32_t* ids, double* weights)
+{
+    const int k = kr + (shared_id >= 0 ? 1 : 0);
+    unsigned char* used = (unsigned char*)malloc((size_t)Er);
+    for (int64_t t = 0; t < M; ++t) {
+        const float* l = logits + t * Er;
+        int32_t* id = ids + t * k;
+        double* wt = weights + t * k;
+        memset(used, 0, (size_t)Er);
+        for (int s = 0; s < kr; ++s) {
+            int best = -1;
+            for (int e = 0; e < Er; ++e)
+                if (!used[e] && (best < 0 || l[e] > l[best])) best = e;
+            used[best] = 1;
+            id[s] = best;
+        }
+        const double top = (double)l[id[0]];
+        double sum = 0.0;
+        for (int s = 0; s < kr; ++s) {
+            wt[s] = exp((double)l[id[s]] - top);
+            sum += wt[s];
+        }
+        for (int s = 0; s < kr; ++s) wt[s] /= sum;
+        if (shared_id >= 0) {
+            id[kr] = shared_id;
+            wt[kr] = 1.0;
+        }
+    }
+    free(used);
+}
+
 int oracle_num_threads(void)
 {
 #ifdef _OPENMP
