@@ -101,6 +101,23 @@ int moe_a8w4_pack_weights(const moe_a8w4_dims* dims, const uint8_t* w13, const u
                           const uint8_t* w2, const uint8_t* w2_s, uint8_t* w13_p, uint8_t* w13_s_p,
                           uint8_t* w2_p, uint8_t* w2_s_p, hipStream_t stream);
 
+/* ------------------------------------------------------------ the router */
+
+/* Router of the backbone configurations (the workloads' "softmax top-k of the
+ * router logits, renormalised"; the prefill configuration's fused shared
+ * expert): for each token, the k_routed largest of its routed_experts logits
+ * in descending order (equal values: the lower expert id first), weighted by
+ * the softmax of the chosen logits -- the softmax over all routed_experts
+ * renormalised over the chosen ones, which is the same in exact arithmetic;
+ * computed in float32 (the ids are exact, the weights within a few ulp).
+ * With shared_expert >= 0 a last slot holds that expert id with weight 1.
+ *   logits        [M, routed_experts] float32
+ *   topk_ids      [M, k] int32 out, k = k_routed + (shared_expert >= 0)
+ *   topk_weights  [M, k] float32 out
+ * Limits: 1 <= k_routed <= routed_experts <= 512, k <= 8. */
+int moe_a8w4_route(int32_t M, int32_t routed_experts, int32_t k_routed, int32_t shared_expert,
+                   const float* logits, int32_t* topk_ids, float* topk_weights, hipStream_t stream);
+
 /* ------------------------------------------------------------- the layer */
 
 /* The whole layer: quantise, sort, stage one, stage two, BF16 output.
@@ -115,6 +132,18 @@ int moe_a8w4_forward(const moe_a8w4_dims* dims, const void* hidden, const int32_
                      const float* topk_weights, const uint8_t* w13_p, const uint8_t* w13_s_p,
                      const uint8_t* w2_p, const uint8_t* w2_s_p, void* out, void* workspace,
                      size_t workspace_bytes, hipStream_t stream);
+
+/* The whole layer from the router logits: moe_a8w4_route (with
+ * routed_experts = dims->routed_experts, k_routed = dims->topk minus the
+ * shared slot), writing topk_ids / topk_weights [M, dims->topk] (caller-owned
+ * outputs, left holding the routing), then moe_a8w4_forward on them.  When
+ * one workgroup sorts and M <= 64, the routing runs inside the sort's launch
+ * (no launch of its own).  Other arguments as moe_a8w4_forward. */
+int moe_a8w4_forward_routed(const moe_a8w4_dims* dims, const void* hidden, const float* router_logits,
+                            int32_t shared_expert, int32_t* topk_ids, float* topk_weights,
+                            const uint8_t* w13_p, const uint8_t* w13_s_p, const uint8_t* w2_p,
+                            const uint8_t* w2_s_p, void* out, void* workspace, size_t workspace_bytes,
+                            hipStream_t stream);
 
 /* ----------------------------------------------- the steps, one at a time */
 

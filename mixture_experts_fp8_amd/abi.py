@@ -28,6 +28,7 @@ EXPORTS = (
     "moe_a8w4_pack_weights", "moe_a8w4_forward", "moe_a8w4_quant_act", "moe_a8w4_sort",
     "moe_a8w4_quant_sort",
     "moe_a8w4_stage1", "moe_a8w4_stage2", "moe_a8w4_combine", "moe_a8w4_status_str",
+    "moe_a8w4_route", "moe_a8w4_forward_routed",
 )
 
 
@@ -73,6 +74,8 @@ def load() -> ctypes.CDLL:
         "moe_a8w4_stage2": (ctypes.c_int, [P, i32] + [vp] * 9 + [vp]),
         "moe_a8w4_combine": (ctypes.c_int, [P, vp, vp, vp, vp]),
         "moe_a8w4_status_str": (ctypes.c_char_p, [ctypes.c_int]),
+        "moe_a8w4_route": (ctypes.c_int, [i32, i32, i32, i32, vp, vp, vp, vp]),
+        "moe_a8w4_forward_routed": (ctypes.c_int, [P, vp, vp, i32] + [vp] * 8 + [sz, vp]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -148,6 +151,42 @@ def moe_a8w4_forward(dims, hidden, topk_ids, topk_weights, w13_p, w13_s_p, w2_p,
                                  _ptr(workspace), workspace.numel(), _stream(stream))
     _check("moe_a8w4_forward", st)
     return out
+
+
+def moe_a8w4_route(logits, k_routed, shared_expert=-1, topk_ids=None, topk_weights=None, stream=None):
+    """(topk_ids int32 [M, k], topk_weights float32 [M, k]) from router logits
+    float32 [M, routed_experts]; k = k_routed + (shared_expert >= 0)."""
+    M, Er = logits.shape
+    k = k_routed + (1 if shared_expert >= 0 else 0)
+    if topk_ids is None:
+        topk_ids = torch.empty((M, k), dtype=torch.int32, device=logits.device)
+    if topk_weights is None:
+        topk_weights = torch.empty((M, k), dtype=torch.float32, device=logits.device)
+    st = load().moe_a8w4_route(M, Er, k_routed, shared_expert, _ptr(logits), _ptr(topk_ids),
+                               _ptr(topk_weights), _stream(stream))
+    _check("moe_a8w4_route", st)
+    return topk_ids, topk_weights
+
+
+def moe_a8w4_forward_routed(dims, hidden, router_logits, shared_expert, w13_p, w13_s_p, w2_p, w2_s_p,
+                            topk_ids=None, topk_weights=None, out=None, workspace=None, stream=None):
+    """(out BF16 [M, H], topk_ids, topk_weights) of the layer routed from its
+    logits [M, dims.routed_experts] (outputs allocated if not given)."""
+    dev = hidden.device
+    if topk_ids is None:
+        topk_ids = torch.empty((dims.tokens, dims.topk), dtype=torch.int32, device=dev)
+    if topk_weights is None:
+        topk_weights = torch.empty((dims.tokens, dims.topk), dtype=torch.float32, device=dev)
+    if out is None:
+        out = torch.empty((dims.tokens, dims.hidden), dtype=torch.bfloat16, device=dev)
+    if workspace is None:
+        workspace = torch.empty(moe_a8w4_workspace_bytes(dims), dtype=torch.uint8, device=dev)
+    st = load().moe_a8w4_forward_routed(ctypes.byref(dims), _ptr(hidden), _ptr(router_logits), shared_expert,
+                                        _ptr(topk_ids), _ptr(topk_weights), _ptr(w13_p), _ptr(w13_s_p),
+                                        _ptr(w2_p), _ptr(w2_s_p), _ptr(out), _ptr(workspace),
+                                        workspace.numel(), _stream(stream))
+    _check("moe_a8w4_forward_routed", st)
+    return out, topk_ids, topk_weights
 
 
 # ------------------------------------------------------------- the steps

@@ -142,18 +142,14 @@ int moe_a8w4_pack_weights(const moe_a8w4_dims* dims, const uint8_t* w13, const u
   return status_of(moe::launch_pack(w2, w2_s, w2_p, w2_s_p, E, H, I, stream));
 }
 
-int moe_a8w4_forward(const moe_a8w4_dims* dims, const void* hidden, const int32_t* topk_ids,
-                     const float* topk_weights, const uint8_t* w13_p, const uint8_t* w13_s_p,
-                     const uint8_t* w2_p, const uint8_t* w2_s_p, void* out, void* workspace,
-                     size_t workspace_bytes, hipStream_t stream) {
-  int st = check_dims(dims);
-  if (st) return st;
-  if (dims->tokens == 0) return MOE_OK;
-  const void* ptrs[9] = {hidden, topk_ids, topk_weights, w13_p, w13_s_p, w2_p, w2_s_p, out, workspace};
-  for (const void* p : ptrs) {
-    if (!p) return MOE_ERR_NULL;
-    if (!aligned(p, 16)) return MOE_ERR_ALIGN;
-  }
+namespace {
+
+// The layer after argument checks: prep (with the router when ra.logits is
+// set; ids then comes from it), stage one, stage two, combine.
+int forward_body(const moe_a8w4_dims* dims, const void* hidden, const int32_t* topk_ids,
+                 const float* topk_weights, const moe::RouteArgs& ra, const uint8_t* w13_p,
+                 const uint8_t* w13_s_p, const uint8_t* w2_p, const uint8_t* w2_s_p, void* out,
+                 void* workspace, size_t workspace_bytes, hipStream_t stream) {
   if (!aligned(workspace, 256)) return MOE_ERR_ALIGN;
   const int bm = choose_bm(dims);
   const Layout L = layout(dims, bm);
@@ -172,7 +168,7 @@ int moe_a8w4_forward(const moe_a8w4_dims* dims, const void* hidden, const int32_
 
   hipError_t e = moe::launch_prep(topk_ids, dims->tokens, dims->topk, dims->num_experts,
                                   dims->expert_offset, bm, sorted, bexp, npad,
-                                  static_cast<const uint16_t*>(hidden), dims->hidden, a_q, a_s, stream);
+                                  static_cast<const uint16_t*>(hidden), dims->hidden, a_q, a_s, ra, stream);
   if (e != hipSuccess) return status_of(e);
   e = moe::launch_stage1(stage1_args(dims, bm, a_q, a_s, sorted, bexp, npad, w13_p, w13_s_p, iq, is),
                          max_blocks, stream);
@@ -185,6 +181,64 @@ int moe_a8w4_forward(const moe_a8w4_dims* dims, const void* hidden, const int32_
                                        y + route_codes_bytes(dims), static_cast<uint16_t*>(out), stream));
 }
 
+// Router dims: 1 <= k_routed <= routed <= kMaxExperts, k_routed + shared
+// slot <= kMaxTopk.
+bool valid_route(int32_t routed, int32_t k_routed, int32_t shared_expert) {
+  if (routed < 1 || routed > moe::kMaxExperts) return false;
+  if (k_routed < 1 || k_routed > routed) return false;
+  return k_routed + (shared_expert >= 0 ? 1 : 0) <= moe::kMaxTopk;
+}
+
+}  // namespace
+
+int moe_a8w4_forward(const moe_a8w4_dims* dims, const void* hidden, const int32_t* topk_ids,
+                     const float* topk_weights, const uint8_t* w13_p, const uint8_t* w13_s_p,
+                     const uint8_t* w2_p, const uint8_t* w2_s_p, void* out, void* workspace,
+                     size_t workspace_bytes, hipStream_t stream) {
+  int st = check_dims(dims);
+  if (st) return st;
+  if (dims->tokens == 0) return MOE_OK;
+  const void* ptrs[9] = {hidden, topk_ids, topk_weights, w13_p, w13_s_p, w2_p, w2_s_p, out, workspace};
+  for (const void* p : ptrs) {
+    if (!p) return MOE_ERR_NULL;
+    if (!aligned(p, 16)) return MOE_ERR_ALIGN;
+  }
+  return forward_body(dims, hidden, topk_ids, topk_weights, moe::RouteArgs{}, w13_p, w13_s_p, w2_p,
+                      w2_s_p, out, workspace, workspace_bytes, stream);
+}
+
+int moe_a8w4_route(int32_t M, int32_t routed_experts, int32_t k_routed, int32_t shared_expert,
+                   const float* logits, int32_t* topk_ids, float* topk_weights, hipStream_t stream) {
+  if (M < 0 || M >= (1 << 24) || !valid_route(routed_experts, k_routed, shared_expert)) return MOE_ERR_DIMS;
+  if (M == 0) return MOE_OK;
+  if (!logits || !topk_ids || !topk_weights) return MOE_ERR_NULL;
+  if (!aligned(logits, 16) || !aligned(topk_ids, 16) || !aligned(topk_weights, 16)) return MOE_ERR_ALIGN;
+  const moe::RouteArgs ra{logits, routed_experts, k_routed, shared_expert, topk_ids, topk_weights};
+  return status_of(moe::launch_route(ra, M, stream));
+}
+
+int moe_a8w4_forward_routed(const moe_a8w4_dims* dims, const void* hidden, const float* router_logits,
+                            int32_t shared_expert, int32_t* topk_ids, float* topk_weights,
+                            const uint8_t* w13_p, const uint8_t* w13_s_p, const uint8_t* w2_p,
+                            const uint8_t* w2_s_p, void* out, void* workspace, size_t workspace_bytes,
+                            hipStream_t stream) {
+  int st = check_dims(dims);
+  if (st) return st;
+  const int32_t k_routed = dims->topk - (shared_expert >= 0 ? 1 : 0);
+  if (!valid_route(dims->routed_experts, k_routed, shared_expert)) return MOE_ERR_DIMS;
+  if (dims->tokens == 0) return MOE_OK;
+  const void* ptrs[11] = {hidden, router_logits, topk_ids, topk_weights, w13_p, w13_s_p,
+                          w2_p, w2_s_p, out, workspace, hidden};
+  for (const void* p : ptrs) {
+    if (!p) return MOE_ERR_NULL;
+    if (!aligned(p, 16)) return MOE_ERR_ALIGN;
+  }
+  const moe::RouteArgs ra{router_logits, dims->routed_experts, k_routed, shared_expert, topk_ids,
+                          topk_weights};
+  return forward_body(dims, hidden, topk_ids, topk_weights, ra, w13_p, w13_s_p, w2_p, w2_s_p, out,
+                      workspace, workspace_bytes, stream);
+}
+
 int moe_a8w4_quant_act(int32_t M, int32_t H, const void* x, uint8_t* q, uint8_t* s,
                        hipStream_t stream) {
   if (M < 0 || H <= 0 || H % 32 != 0) return MOE_ERR_DIMS;
@@ -192,7 +246,7 @@ int moe_a8w4_quant_act(int32_t M, int32_t H, const void* x, uint8_t* q, uint8_t*
   if (!x || !q || !s) return MOE_ERR_NULL;
   if (!aligned(x, 16) || !aligned(q, 16)) return MOE_ERR_ALIGN;
   return status_of(moe::launch_prep(nullptr, M, 1, 1, 0, 16, nullptr, nullptr, nullptr,
-                                     static_cast<const uint16_t*>(x), H, q, s, stream));
+                                     static_cast<const uint16_t*>(x), H, q, s, moe::RouteArgs{}, stream));
 }
 
 int moe_a8w4_sort(const moe_a8w4_dims* dims, int32_t block_m, const int32_t* topk_ids,
@@ -205,7 +259,7 @@ int moe_a8w4_sort(const moe_a8w4_dims* dims, int32_t block_m, const int32_t* top
   if (dims->tokens > 0 && (!topk_ids || !sorted_ids || !block_expert)) return MOE_ERR_NULL;
   return status_of(moe::launch_prep(topk_ids, dims->tokens, dims->topk, dims->num_experts,
                                     dims->expert_offset, block_m, sorted_ids, block_expert,
-                                    num_padded, nullptr, 0, nullptr, nullptr, stream));
+                                    num_padded, nullptr, 0, nullptr, nullptr, moe::RouteArgs{}, stream));
 }
 
 int moe_a8w4_quant_sort(const moe_a8w4_dims* dims, int32_t block_m, const void* hidden,
@@ -222,7 +276,7 @@ int moe_a8w4_quant_sort(const moe_a8w4_dims* dims, int32_t block_m, const void* 
   return status_of(moe::launch_prep(topk_ids, dims->tokens, dims->topk, dims->num_experts,
                                     dims->expert_offset, block_m, sorted_ids, block_expert,
                                     num_padded, static_cast<const uint16_t*>(hidden), dims->hidden,
-                                    a_q, a_s, stream));
+                                    a_q, a_s, moe::RouteArgs{}, stream));
 }
 
 int moe_a8w4_stage1(const moe_a8w4_dims* dims, int32_t block_m, const uint8_t* a_q,

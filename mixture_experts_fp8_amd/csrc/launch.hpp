@@ -27,11 +27,25 @@ struct GemmArgs {
   uint8_t* y_exps;        //          and their exponent bytes [M, topk, N/32]
 };
 
-// One launch: workgroup 0 sorts the routes (skipped if ids is null), the
-// others quantise x [M, H] (skipped if x is null).
+// Router inputs and outputs (softmax top-k of the logits, optional shared slot).
+struct RouteArgs {
+  const float* logits;    // [M, routed] router logits; null: the ids are given
+  int32_t routed;         // logits per token
+  int32_t k_routed;       // routed slots per token
+  int32_t shared;         // expert id of the extra shared slot, or -1
+  int32_t* ids;           // [M, k_routed + (shared >= 0)] out
+  float* weights;         // same shape, out
+};
+
+// One launch: the first workgroups sort the routes (skipped if ids is null),
+// the others quantise x [M, H] (skipped if x is null).  With ra.logits set the
+// routes come from the router (ids = ra.ids): inside the sort workgroup when
+// a single one sorts, else in a launch of its own before.
 hipError_t launch_prep(const int32_t* ids, int32_t M, int32_t topk, int32_t E, int32_t expert_offset,
                        int32_t bm, int32_t* sorted_ids, int32_t* block_expert, int32_t* num_padded,
-                       const uint16_t* x, int64_t H, uint8_t* q, uint8_t* s, hipStream_t stream);
+                       const uint16_t* x, int64_t H, uint8_t* q, uint8_t* s, const RouteArgs& ra,
+                       hipStream_t stream);
+hipError_t launch_route(const RouteArgs& ra, int32_t M, hipStream_t stream);
 hipError_t launch_combine(int64_t M, int32_t H, int32_t topk, int32_t E, int32_t expert_offset,
                           const int32_t* ids, const int16_t* y_codes, const uint8_t* y_exps,
                           uint16_t* out, hipStream_t stream);

@@ -66,7 +66,7 @@ __device__ __forceinline__ void wave_sync() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
-__device__ void sort_chunk(SortSmem& sm, const int32_t* __restrict__ ids, int M, int topk, int E,
+__device__ void sort_chunk(SortSmem& sm, const int32_t* ids, int M, int topk, int E,
                            int expert_offset, int bm, int chunk, int nchunks,
                            int32_t* __restrict__ sorted_ids, int32_t* __restrict__ block_expert,
                            int32_t* __restrict__ num_padded) {
@@ -235,19 +235,96 @@ __device__ void quant_range(const uint16_t* __restrict__ x, uint8_t* __restrict_
   for (; i < n8; i += stride) quant_one(*reinterpret_cast<const uint4*>(x + i * 8), i, q, s);
 }
 
+// Router (backbone configurations: softmax top-k of the router logits,
+// renormalised; the prefill configuration's fused shared expert in a last
+// slot with weight 1).  One wave per token: lane l holds logits l, l + 64,
+// ...; k rounds of a wave-wide arg-max (equal values: the lower expert id),
+// then the weights as the softmax of the chosen logits -- the full softmax
+// renormalised over the chosen ones, which is the same in exact arithmetic.
+constexpr int kRouterPerLane = kMaxExperts / kWave;
+// tokens the sort workgroup routes itself (four per wave) before sorting
+constexpr int kRouteInSortTokens = 4 * kSortWaves;
+
+__device__ void route_token(const RouteArgs& ra, int64_t t) {
+  const int lane = threadIdx.x & 63;
+  const int Er = ra.routed, kr = ra.k_routed;
+  const int k = kr + (ra.shared >= 0 ? 1 : 0);
+  const float* l = ra.logits + t * Er;
+  float v[kRouterPerLane];
+  uint32_t avail = 0;
+#pragma unroll
+  for (int i = 0; i < kRouterPerLane; ++i) {
+    const int e = lane + kWave * i;
+    v[i] = e < Er ? l[e] : 0.f;
+    if (e < Er) avail |= 1u << i;
+  }
+  constexpr int kNone = 0x7FFFFFFF;
+  float my_v = 0.f, top0 = 0.f, ex = 0.f, sum = 0.f;
+  int my_id = 0;
+  for (int s = 0; s < kr; ++s) {
+    float bv = 0.f;
+    int bi = kNone;
+#pragma unroll
+    for (int i = 0; i < kRouterPerLane; ++i)   // ascending id: > keeps the lower one
+      if (((avail >> i) & 1u) && (bi == kNone || v[i] > bv)) {
+        bv = v[i];
+        bi = lane + kWave * i;
+      }
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) {
+      const float ov = __shfl_xor(bv, off);
+      const int oi = __shfl_xor(bi, off);
+      if (oi != kNone && (bi == kNone || ov > bv || (ov == bv && oi < bi))) {
+        bv = ov;
+        bi = oi;
+      }
+    }
+    if ((bi & (kWave - 1)) == lane) avail &= ~(1u << (bi / kWave));
+    if (s == 0) top0 = bv;
+    const float es = expf(bv - top0);   // every lane: the sum runs in slot order
+    sum += es;
+    if (lane == s) {
+      my_v = es;
+      my_id = bi;
+    }
+  }
+  ex = my_v;
+  if (lane < kr) {
+    ra.ids[t * k + lane] = my_id;
+    ra.weights[t * k + lane] = ex / sum;
+  } else if (lane == kr && ra.shared >= 0) {
+    ra.ids[t * k + kr] = ra.shared;
+    ra.weights[t * k + kr] = 1.0f;
+  }
+}
+
+__global__ void __launch_bounds__(256) route_kernel(RouteArgs ra, int M) {
+  const int64_t t = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (t < M) route_token(ra, t);
+}
+
 int quant_blocks(int64_t n8) {
   int64_t b = (n8 + kPrepThreads - 1) / kPrepThreads;
   return (int)(b > 1024 ? 1024 : b);
 }
 
-// Workgroups 0 .. ns-1 sort (ns = 0 without ids); the others quantise.
+// Workgroups 0 .. ns-1 sort (ns = 0 without ids); the others quantise.  With
+// ra.logits set (and ns = 1) the sort workgroup first routes every token,
+// writing the ids it then sorts.
 __global__ void __launch_bounds__(kPrepThreads) prep_kernel(
-    const int32_t* __restrict__ ids, int M, int topk, int E, int expert_offset, int bm, int ns,
+    const int32_t* ids, int M, int topk, int E, int expert_offset, int bm, int ns,
     int32_t* __restrict__ sorted_ids, int32_t* __restrict__ block_expert,
     int32_t* __restrict__ num_padded, const uint16_t* __restrict__ x, uint8_t* __restrict__ q,
-    uint8_t* __restrict__ s, int64_t n8) {
+    uint8_t* __restrict__ s, int64_t n8, RouteArgs ra) {
   __shared__ SortSmem sm;
   if ((int)blockIdx.x < ns) {
+    if (ra.logits) {
+      for (int t = threadIdx.x >> 6; t < M; t += kSortWaves) route_token(ra, t);
+      // the ids are read back by this workgroup only
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+      __syncthreads();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+    }
     sort_chunk(sm, ids, M, topk, E, expert_offset, bm, blockIdx.x, ns, sorted_ids, block_expert,
                num_padded);
     return;
@@ -258,15 +335,33 @@ __global__ void __launch_bounds__(kPrepThreads) prep_kernel(
 
 }  // namespace
 
+hipError_t launch_route(const RouteArgs& ra, int32_t M, hipStream_t stream) {
+  if (M <= 0) return hipSuccess;
+  hipLaunchKernelGGL(route_kernel, dim3((unsigned)((M + 3) / 4)), dim3(256), 0, stream, ra, M);
+  return hipGetLastError();
+}
+
 hipError_t launch_prep(const int32_t* ids, int32_t M, int32_t topk, int32_t E, int32_t expert_offset,
                        int32_t bm, int32_t* sorted_ids, int32_t* block_expert, int32_t* num_padded,
-                       const uint16_t* x, int64_t H, uint8_t* q, uint8_t* s, hipStream_t stream) {
+                       const uint16_t* x, int64_t H, uint8_t* q, uint8_t* s, const RouteArgs& ra,
+                       hipStream_t stream) {
   const int64_t n8 = x ? (int64_t)M * H / 8 : 0;
+  RouteArgs fused = ra;
+  if (ra.logits) {
+    ids = ra.ids;
+    if (sort_blocks((int64_t)M * topk) > 1 || M > kRouteInSortTokens) {
+      // several sort workgroups each read every id, or more tokens than the
+      // sort workgroup's waves route quickly: route first
+      hipError_t e = launch_route(ra, M, stream);
+      if (e != hipSuccess) return e;
+      fused.logits = nullptr;
+    }
+  }
   const int ns = ids ? sort_blocks((int64_t)M * topk) : 0;
   const int grid = ns + (n8 > 0 ? quant_blocks(n8) : 0);
   if (grid == 0) return hipSuccess;
   hipLaunchKernelGGL(prep_kernel, dim3(grid), dim3(kPrepThreads), 0, stream, ids, M, topk, E,
-                     expert_offset, bm, ns, sorted_ids, block_expert, num_padded, x, q, s, n8);
+                     expert_offset, bm, ns, sorted_ids, block_expert, num_padded, x, q, s, n8, fused);
   return hipGetLastError();
 }
 

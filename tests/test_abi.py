@@ -100,7 +100,7 @@ def test_block_m_capacity_and_workspace_sizes():
     with pytest.raises(abi.MoeError):
         abi.moe_a8w4_sort_capacity(d, 48)
     ws = abi.moe_a8w4_workspace_bytes(dims(tokens=16384, num_experts=385, topk=7))
-    assert ws < 4 << 30     # dominated by the [M, topk, H] fp32 route outputs
+    assert ws < 2 << 30     # dominated by the [M, topk, H] 16-bit route rows
     assert "block_m" in abi.status_str(abi.MOE_ERR_BLOCK_M)
 
 
@@ -116,3 +116,28 @@ def test_step_entry_points_validate():
     assert lib.moe_a8w4_combine(ctypes.byref(d), p, p, None, None) == abi.MOE_ERR_NULL
     assert lib.moe_a8w4_combine(ctypes.byref(d), p, ctypes.c_void_p(4100), p, None) == abi.MOE_ERR_ALIGN
     assert lib.moe_a8w4_pack_weights(ctypes.byref(d), *([p] * 7), None, None) == abi.MOE_ERR_NULL
+
+
+def test_router_entry_points_validate():
+    """Bad router dims, null or misaligned pointers: a status, nothing launched."""
+    lib = abi.load()
+    p, odd = ctypes.c_void_p(4096), ctypes.c_void_p(4100)
+    assert lib.moe_a8w4_route(4, 384, 0, -1, p, p, p, None) == abi.MOE_ERR_DIMS      # no routed slot
+    assert lib.moe_a8w4_route(4, 5, 6, -1, p, p, p, None) == abi.MOE_ERR_DIMS        # k > experts
+    assert lib.moe_a8w4_route(4, 384, 8, 384, p, p, p, None) == abi.MOE_ERR_DIMS     # 9 slots
+    assert lib.moe_a8w4_route(4, 513, 6, -1, p, p, p, None) == abi.MOE_ERR_DIMS      # > 512 logits
+    assert lib.moe_a8w4_route(-1, 384, 6, -1, p, p, p, None) == abi.MOE_ERR_DIMS
+    assert lib.moe_a8w4_route(0, 384, 6, -1, None, None, None, None) == abi.MOE_OK
+    assert lib.moe_a8w4_route(4, 384, 6, -1, None, p, p, None) == abi.MOE_ERR_NULL
+    assert lib.moe_a8w4_route(4, 384, 6, -1, odd, p, p, None) == abi.MOE_ERR_ALIGN
+    d = dims(tokens=4, num_experts=16, topk=6)
+    d.routed_experts = 16
+    assert lib.moe_a8w4_forward_routed(ctypes.byref(d), p, None, -1, *([p] * 8), 1 << 30, None) \
+        == abi.MOE_ERR_NULL
+    d.routed_experts = 0                                                              # no logits width
+    assert lib.moe_a8w4_forward_routed(ctypes.byref(d), p, p, -1, *([p] * 8), 1 << 30, None) \
+        == abi.MOE_ERR_DIMS
+    d.routed_experts = 16
+    d.topk = 1                                                                        # shared slot only
+    assert lib.moe_a8w4_forward_routed(ctypes.byref(d), p, p, 15, *([p] * 8), 1 << 30, None) \
+        == abi.MOE_ERR_DIMS
