@@ -59,6 +59,9 @@ def parse():
     ap.add_argument("--local-slice-table", action="store_true",
                     help="instead of the decode sweep: one call per token count of the local-slice "
                          "workload (the pages' own MI355X fused_moe timing table) as a JSON line")
+    ap.add_argument("--router-table", action="store_true",
+                    help="instead of the decode sweep: per backbone decode bucket, the router alone, "
+                         "the layer from given routes and the layer from router logits (JSON line)")
     return ap.parse_args()
 
 
@@ -146,6 +149,65 @@ def local_slice_table(args):
                       "rows": rows, "geomean_speedup_vs_pages": round(geo, 3)}))
 
 
+def _timed_us(fn, steps):
+    """Median microseconds of fn() over max(3, steps) calls, each behind a spin
+    kernel so that host launch latency stays out of the event interval."""
+    import torch
+    ts = []
+    for _ in range(max(3, steps)):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda._sleep(HOST_COVER_CYCLES)
+        e0.record()
+        fn()
+        e1.record()
+        e1.synchronize()
+        ts.append(e0.elapsed_time(e1) * 1e3)
+    return float(np.median(ts))
+
+
+def router_table(args):
+    """Backbone decode buckets: microseconds of the router alone, of the layer
+    from given routes (moe_a8w4_forward) and from router logits
+    (moe_a8w4_forward_routed, the router inside the sort's launch up to 16
+    tokens)."""
+    import torch
+    from mixture_experts_fp8_amd import abi, workloads as wl
+    dev = torch.device("cuda:0")
+    w = wl.WORKLOADS["backbone-decode"]
+    host_w = wl.make_weights(w)
+    d1 = abi.make_dims(1, w.hidden, w.inter, w.num_experts, w.topk)
+    raw = [torch.from_numpy(np.ascontiguousarray(x)).to(dev) for x in host_w]
+    packed = abi.moe_a8w4_pack_weights(d1, *raw)
+    del raw, host_w
+    rows = {}
+    for M in (6, 12, 24, 48, 96, 192, 384, 768):
+        rng = np.random.default_rng([w.config_id, 9, M])
+        hidden = wl.make_hidden(rng, M, w.hidden)
+        logits = torch.from_numpy(rng.standard_normal((M, w.routed_experts), dtype=np.float32)).to(dev)
+        d = abi.make_dims(M, w.hidden, w.inter, w.num_experts, w.topk, w.expert_offset, w.routed_experts)
+        x = torch.from_numpy(hidden.view(np.int16)).to(dev).view(torch.bfloat16)
+        ids = torch.empty((M, w.topk), dtype=torch.int32, device=dev)
+        wts = torch.empty((M, w.topk), dtype=torch.float32, device=dev)
+        out = torch.empty((M, w.hidden), dtype=torch.bfloat16, device=dev)
+        ws = torch.empty(abi.moe_a8w4_workspace_bytes(d), dtype=torch.uint8, device=dev)
+        route = lambda: abi.moe_a8w4_route(logits, w.topk, -1, ids, wts)
+        fwd = lambda: abi.moe_a8w4_forward(d, x, ids, wts, *packed, out=out, workspace=ws)
+        routed = lambda: abi.moe_a8w4_forward_routed(d, x, logits, -1, *packed, topk_ids=ids,
+                                                     topk_weights=wts, out=out, workspace=ws)
+        for _ in range(args.warmup):
+            routed()
+        torch.cuda.synchronize()
+        r = dict(router_us=round(_timed_us(route, args.steps), 1), forward_us=round(_timed_us(fwd, args.steps), 1),
+                 forward_routed_us=round(_timed_us(routed, args.steps), 1))
+        r["routing_cost_us"] = round(r["forward_routed_us"] - r["forward_us"], 1)
+        rows[str(M)] = r
+        print("M=%4d  %s" % (M, r), file=sys.stderr, flush=True)
+    print(json.dumps({"table": "router and layer, backbone decode buckets, one MI355X", "unit": "us/call",
+                      "config": {"workload": "backbone decode sweep: H5120, 384 experts, top-6, I640; "
+                                             "router logits N(0,1)"},
+                      "rows": rows}))
+
+
 def measured_traffic():
     """Stage-one HBM bytes per launch from the committed counter summary, or None
     if the kernel sources changed since those counters were taken."""
@@ -193,6 +255,9 @@ def main():
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     if args.local_slice_table:
         local_slice_table(args)
+        return
+    if args.router_table:
+        router_table(args)
         return
     if args.profile_call:
         profile_call(args)

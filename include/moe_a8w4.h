@@ -137,7 +137,7 @@ int moe_a8w4_forward(const moe_a8w4_dims* dims, const void* hidden, const int32_
  * routed_experts = dims->routed_experts, k_routed = dims->topk minus the
  * shared slot), writing topk_ids / topk_weights [M, dims->topk] (caller-owned
  * outputs, left holding the routing), then moe_a8w4_forward on them.  When
- * one workgroup sorts and M <= 64, the routing runs inside the sort's launch
+ * one workgroup sorts and M <= 16, the routing runs inside the sort's launch
  * (no launch of its own).  Other arguments as moe_a8w4_forward. */
 int moe_a8w4_forward_routed(const moe_a8w4_dims* dims, const void* hidden, const float* router_logits,
                             int32_t shared_expert, int32_t* topk_ids, float* topk_weights,

@@ -242,8 +242,10 @@ __device__ void quant_range(const uint16_t* __restrict__ x, uint8_t* __restrict_
 // then the weights as the softmax of the chosen logits -- the full softmax
 // renormalised over the chosen ones, which is the same in exact arithmetic.
 constexpr int kRouterPerLane = kMaxExperts / kWave;
-// tokens the sort workgroup routes itself (four per wave) before sorting
-constexpr int kRouteInSortTokens = 4 * kSortWaves;
+// tokens the sort workgroup routes itself (one per wave) before sorting; for
+// more, a launch of its own (a wave per token) costs less than the waves of
+// one workgroup routing several tokens each
+constexpr int kRouteInSortTokens = kSortWaves;
 
 __device__ void route_token(const RouteArgs& ra, int64_t t) {
   const int lane = threadIdx.x & 63;

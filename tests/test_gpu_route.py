@@ -46,9 +46,11 @@ def test_route_ties_take_the_lower_id():
 
 
 @pytest.mark.parametrize("name,E,routed,topk,shared,M", [
-    ("backbone-decode", 16, 16, 6, -1, 33),     # routing inside the sort launch
-    ("backbone-decode", 16, 16, 6, -1, 300),    # routing in a launch of its own
-    ("prefill-shared", 9, 8, 3, 8, 48),         # two routed slots and the shared expert
+    ("backbone-decode", 16, 16, 6, -1, 13),     # routing inside the sort launch
+    ("backbone-decode", 16, 16, 6, -1, 33),     # routing in a launch of its own
+    ("backbone-decode", 16, 16, 6, -1, 300),    # the same, several sort workgroups
+    ("prefill-shared", 9, 8, 3, 8, 12),         # two routed slots and the shared expert, in the sort
+    ("prefill-shared", 9, 8, 3, 8, 48),         # the same, routed first
 ])
 def test_forward_routed(name, E, routed, topk, shared, M):
     w = wl.scaled(wl.WORKLOADS[name], num_experts=E, routed_experts=routed, topk=topk,
