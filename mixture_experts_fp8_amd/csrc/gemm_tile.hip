@@ -57,23 +57,8 @@ typedef __attribute__((address_space(3))) void* lds_ptr;
 // assembly so that the compiler, which cannot tell the ring's slots apart,
 // does not wait for every load in flight before each LDS read; the kernel
 // waits for them itself (vmcnt) before the barrier that publishes a slot.
-#ifndef MOE_TILE_AMOD
-#define MOE_TILE_AMOD ""
-#endif
-#ifndef MOE_TILE_BMOD
-#define MOE_TILE_BMOD ""
-#endif
 __device__ __forceinline__ void dma16(const void* g, uint32_t lds) {
   asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(g), "s"(lds)
-               : "memory", "m0");
-}
-// the same with cache-policy bits appended (weights stream once per slice)
-__device__ __forceinline__ void dma16_a(const void* g, uint32_t lds) {
-  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off " MOE_TILE_AMOD ::"v"(g), "s"(lds)
-               : "memory", "m0");
-}
-__device__ __forceinline__ void dma16_b(const void* g, uint32_t lds) {
-  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off " MOE_TILE_BMOD ::"v"(g), "s"(lds)
                : "memory", "m0");
 }
 __device__ __forceinline__ void dma4(const void* g, uint32_t lds) {
@@ -227,9 +212,9 @@ __global__ void __launch_bounds__(64 * (kComputeWaves + kLoaderWaves), 3) tile_k
       const uint32_t base = lds0 + (uint32_t)(s % S) * G::BYTES;
 #pragma unroll
       for (int t = 0; t < 4; ++t)
-        dma16_a(gA + (int64_t)s * 4096 + t * 1024, base + G::A + l * 4096 + t * 1024);
+        dma16(gA + (int64_t)s * 4096 + t * 1024, base + G::A + l * 4096 + t * 1024);
 #pragma unroll
-      for (int i = 0; i < G::NBCH; ++i) dma16_b(gB[i] + s * 128, base + G::B + (l * G::NBCH + i) * 1024);
+      for (int i = 0; i < G::NBCH; ++i) dma16(gB[i] + s * 128, base + G::B + (l * G::NBCH + i) * 1024);
       dma4(gAs + (int64_t)s * 256, base + G::AS + l * 256);
       if (has_bs) dma4(gBs + 4 * s, base + G::BS + l * 256);
     };
@@ -458,7 +443,7 @@ __global__ void __launch_bounds__(64 * (kComputeWaves + kLoaderWaves), 3) tile_r
       const int piece = (lane & 7) ^ ((t >> 1) & 7);
       const uint8_t* src = args.bq + brow(t) * K + piece * 16;
       const uint32_t dst = lds_addr(&sB[0]) + (uint32_t)(l * NBCH + i) * 1024;
-      for (int ks = 0; ks < KS; ++ks) dma16_b(src + ks * 128, dst + (uint32_t)ks * BM * 128);
+      for (int ks = 0; ks < KS; ++ks) dma16(src + ks * 128, dst + (uint32_t)ks * BM * 128);
     }
     {
       // token scales as one flat run of BM * KS words (word d: token d / KS,
@@ -486,7 +471,7 @@ __global__ void __launch_bounds__(64 * (kComputeWaves + kLoaderWaves), 3) tile_r
       const int64_t step = (int64_t)j * 4 * KS + ks;   // row group advances by 4 per slice
       const uint32_t base = lds0 + (uint32_t)(q % S) * SLOT;
 #pragma unroll
-      for (int t = 0; t < 4; ++t) dma16_a(gA + step * 4096 + t * 1024, base + l * 4096 + t * 1024);
+      for (int t = 0; t < 4; ++t) dma16(gA + step * 4096 + t * 1024, base + l * 4096 + t * 1024);
       dma4(gAs + step * 256, base + 16384 + l * 256);
     };
 #pragma unroll
