@@ -236,9 +236,16 @@ hipError_t launch_stage1(const GemmArgs& a, int64_t max_blocks, hipStream_t stre
   }
 }
 
+// Stage two splits K over the four waves of a workgroup when K is long (I =
+// 2304: 18 steps) and blocks hold at most 16 routes: one wave per row group
+// would walk 18 steps of dependent loads, and such a call has too few blocks
+// to hide that behind other workgroups (local slice, 1 token: 38 -> 31 us).
+// At I = 640 (5 steps), or with blocks of 32, a split measured no gain.
 hipError_t launch_stage2(const GemmArgs& a, int64_t max_blocks, hipStream_t stream) {
   switch (a.bm) {
-    case 16: return launch_gemm<2, 1, 1, MOE_S2_PD, MOE_NT_SMALL>(a, max_blocks, stream);
+    case 16:
+      return a.K >= 1024 ? launch_gemm<2, 1, 4, MOE_S2_PD, MOE_NT_SMALL>(a, max_blocks, stream)
+                         : launch_gemm<2, 1, 1, MOE_S2_PD, MOE_NT_SMALL>(a, max_blocks, stream);
     case 32: return launch_gemm<2, 2, 1, MOE_S2_PD, MOE_NT_SMALL>(a, max_blocks, stream);
     case 64:
     case 128: return launch_tile(2, a, max_blocks, stream);

@@ -223,7 +223,8 @@ def test_combine_route_rows_bit_exact():
     assert not got[3].any()
 
 
-@pytest.mark.parametrize("name,M,E", [("draft-decode", 33, 8), ("local-slice", 40, 6),
+@pytest.mark.parametrize("name,M,E", [("draft-decode", 33, 8), ("local-slice", 8, 6),
+                                      ("local-slice", 12, 6), ("local-slice", 40, 6),
                                       ("local-slice", 80, 6)])
 def test_stage2_route_rows(name, M, E):
     """Stage two given the GPU's own intermediate, route by route: decoded rows
