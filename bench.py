@@ -59,6 +59,9 @@ def parse():
     ap.add_argument("--local-slice-table", action="store_true",
                     help="instead of the decode sweep: one call per token count of the local-slice "
                          "workload (the pages' own MI355X fused_moe timing table) as a JSON line")
+    ap.add_argument("--fused-table", action="store_true",
+                    help="instead of the decode sweep: per decode bucket, the layer as four launches "
+                         "against the fused decode launch")
     ap.add_argument("--router-table", action="store_true",
                     help="instead of the decode sweep: per backbone decode bucket, the router alone, "
                          "the layer from given routes and the layer from router logits (JSON line)")
@@ -165,6 +168,67 @@ def _timed_us(fn, steps):
     return float(np.median(ts))
 
 
+def fused_table(args):
+    """Backbone decode buckets: microseconds per call of the layer as four
+    launches (moe_a8w4_forward) and as two (moe_a8w4_quant_sort, then
+    moe_a8w4_stages_fused: stage one, stage two and the combine in one
+    launch).  Calls rotate over four copies of the weights so that each
+    streams its experts from HBM."""
+    import torch
+    from mixture_experts_fp8_amd import abi, workloads as wl
+    dev = torch.device("cuda:0")
+    w = wl.WORKLOADS["backbone-decode"]
+    host_w = wl.make_weights(w)
+    d1 = abi.make_dims(1, w.hidden, w.inter, w.num_experts, w.topk)
+    raw = [torch.from_numpy(np.ascontiguousarray(x)).to(dev) for x in host_w]
+    p0 = abi.moe_a8w4_pack_weights(d1, *raw)
+    copies = [p0] + [tuple(t.clone() for t in p0) for _ in range(3)]
+    del raw, host_w
+    rows = {}
+    for M in BUCKETS:
+        hidden, ids, wts = wl.make_inputs(w, M, "softmax")
+        d = abi.make_dims(M, w.hidden, w.inter, w.num_experts, w.topk, w.expert_offset, w.routed_experts)
+        bm = abi.moe_a8w4_block_m(d)
+        x = torch.from_numpy(hidden.view(np.int16)).to(dev).view(torch.bfloat16)
+        idd = torch.from_numpy(ids).to(dev)
+        wd = torch.from_numpy(wts).to(dev)
+        out = torch.empty((M, w.hidden), dtype=torch.bfloat16, device=dev)
+        ws = torch.empty(abi.moe_a8w4_workspace_bytes(d), dtype=torch.uint8, device=dev)
+        q, s_, srt, bexp, npad = abi.moe_a8w4_quant_sort(d, bm, x, idd)
+        cnt = torch.zeros(abi.moe_a8w4_fused_counters(d, bm), dtype=torch.int32, device=dev)
+        iq, is_, y, out2 = abi.moe_a8w4_stages_fused(d, bm, q, s_, srt, bexp, npad, idd, wd, *copies[0], cnt)
+        turn = [0]
+
+        def nxt():
+            turn[0] += 1
+            return copies[turn[0] % len(copies)]
+
+        def four():
+            abi.moe_a8w4_forward(d, x, idd, wd, *nxt(), out=out, workspace=ws)
+
+        def two():
+            abi.moe_a8w4_quant_sort(d, bm, x, idd)
+            abi.moe_a8w4_stages_fused(d, bm, q, s_, srt, bexp, npad, idd, wd, *nxt(), cnt, inter_q=iq,
+                                      inter_s=is_, y_routes=y, out=out2)
+
+        for _ in range(args.warmup):
+            four()
+            two()
+        torch.cuda.synchronize()
+        a = algorithmic(w, M, ids)
+        t4, t2 = _timed_us(four, args.steps), _timed_us(two, args.steps)
+        if int(cnt[0]) != 0:
+            raise RuntimeError("fused launch: a wait gave up (status word set)")
+        rows[str(M)] = dict(block_m=bm, four_launches_us=round(t4, 1), fused_us=round(t2, 1),
+                            four_launches_hbm_frac=round(a["bytes"] / t4 / 1e3 / HBM_PEAK_GBS, 3),
+                            fused_hbm_frac=round(a["bytes"] / t2 / 1e3 / HBM_PEAK_GBS, 3))
+        print("M=%4d  %s" % (M, rows[str(M)]), file=sys.stderr, flush=True)
+    print(json.dumps({"table": "four launches vs fused decode launch, backbone decode buckets, one MI355X",
+                      "unit": "us/call",
+                      "config": {"workload": "backbone decode sweep: H5120, 384 experts, top-6, I640"},
+                      "rows": rows}))
+
+
 def router_table(args):
     """Backbone decode buckets: microseconds of the router alone, of the layer
     from given routes (moe_a8w4_forward) and from router logits
@@ -258,6 +322,9 @@ def main():
         return
     if args.router_table:
         router_table(args)
+        return
+    if args.fused_table:
+        fused_table(args)
         return
     if args.profile_call:
         profile_call(args)

@@ -120,7 +120,8 @@ int moe_a8w4_route(int32_t M, int32_t routed_experts, int32_t k_routed, int32_t 
 
 /* ------------------------------------------------------------- the layer */
 
-/* The whole layer: quantise, sort, stage one, stage two, BF16 output.
+/* The whole layer: quantise, sort, stage one, stage two, BF16 output, as
+ * four launches (quantiser with the sort, stage one, stage two, combine). 
  *   hidden        [M, H] BF16
  *   topk_ids      [M, topk] int32 global expert ids (any value; non-local skipped)
  *   topk_weights  [M, topk] float32
@@ -201,6 +202,35 @@ int moe_a8w4_stage2(const moe_a8w4_dims* dims, int32_t block_m, const uint8_t* i
  * slots are local); zero for a token without one.  Bitwise repeatable. */
 int moe_a8w4_combine(const moe_a8w4_dims* dims, const int32_t* topk_ids, const void* y_routes,
                      void* out, hipStream_t stream);
+
+/* Stage one, stage two and the top-k combine of one call in a single launch
+ * (block_m 16 or 32), the decode form of the layer after moe_a8w4_quant_sort
+ * (aiter PR 5904, "Fused-MoE kernel, expert-parallel benchmark": one call
+ * holds sorting, both stages and the intermediate quantization).  Results as
+ * moe_a8w4_stage1 (inter_q, inter_s), moe_a8w4_stage2 (y_routes) and
+ * moe_a8w4_combine (out, every element written) with the same buffers.
+ * A stage-two tile of a block starts streaming its weights at once and waits
+ * for that block's stage-one tiles through counters in device memory; the
+ * workgroup that finishes a token's last route over a range of output
+ * columns sums that range.
+ *   counters  int32 [moe_a8w4_fused_counters(dims, block_m)], caller-owned:
+ *             must hold zeros on entry; a completed call leaves them zero.
+ *             counters[0] is a status word: nonzero if a wait gave up after
+ *             about 0.5 s (only possible when the GPU cannot run all of the
+ *             launch's earlier workgroups, e.g. it is shared), in which case
+ *             the outputs and counters are invalid.
+ * Calls sharing a counters buffer must not overlap.  Entries past
+ * num_padded of the sort buffers are ignored. */
+int moe_a8w4_stages_fused(const moe_a8w4_dims* dims, int32_t block_m, const uint8_t* a_q,
+                          const uint8_t* a_s, const int32_t* sorted_ids, const int32_t* block_expert,
+                          const int32_t* num_padded, const int32_t* topk_ids, const float* topk_weights,
+                          const uint8_t* w13_p, const uint8_t* w13_s_p, const uint8_t* w2_p,
+                          const uint8_t* w2_s_p, uint8_t* inter_q, uint8_t* inter_s, void* y_routes,
+                          int32_t* counters, void* out, hipStream_t stream);
+
+/* Number of int32 counters moe_a8w4_stages_fused needs (negative status on
+ * invalid dims, or block_m other than 16 and 32). */
+int64_t moe_a8w4_fused_counters(const moe_a8w4_dims* dims, int32_t block_m);
 
 /* Name of a status code (static string). */
 const char* moe_a8w4_status_str(int status);

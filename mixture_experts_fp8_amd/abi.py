@@ -28,7 +28,7 @@ EXPORTS = (
     "moe_a8w4_pack_weights", "moe_a8w4_forward", "moe_a8w4_quant_act", "moe_a8w4_sort",
     "moe_a8w4_quant_sort",
     "moe_a8w4_stage1", "moe_a8w4_stage2", "moe_a8w4_combine", "moe_a8w4_status_str",
-    "moe_a8w4_route", "moe_a8w4_forward_routed",
+    "moe_a8w4_route", "moe_a8w4_forward_routed", "moe_a8w4_stages_fused", "moe_a8w4_fused_counters",
 )
 
 
@@ -76,6 +76,8 @@ def load() -> ctypes.CDLL:
         "moe_a8w4_status_str": (ctypes.c_char_p, [ctypes.c_int]),
         "moe_a8w4_route": (ctypes.c_int, [i32, i32, i32, i32, vp, vp, vp, vp]),
         "moe_a8w4_forward_routed": (ctypes.c_int, [P, vp, vp, i32] + [vp] * 8 + [sz, vp]),
+        "moe_a8w4_stages_fused": (ctypes.c_int, [P, i32] + [vp] * 16 + [vp]),
+        "moe_a8w4_fused_counters": (ctypes.c_int64, [P, i32]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -266,6 +268,38 @@ def moe_a8w4_stage2(dims, block_m, inter_q, inter_s, sorted_ids, block_expert, n
                                 _stream(stream))
     _check("moe_a8w4_stage2", st)
     return y_routes
+
+
+def moe_a8w4_fused_counters(dims, block_m) -> int:
+    n = load().moe_a8w4_fused_counters(ctypes.byref(dims), block_m)
+    if n < 0:
+        raise MoeError("moe_a8w4_fused_counters", n)
+    return n
+
+
+def moe_a8w4_stages_fused(dims, block_m, a_q, a_s, sorted_ids, block_expert, num_padded, topk_ids,
+                          topk_weights, w13_p, w13_s_p, w2_p, w2_s_p, counters, inter_q=None,
+                          inter_s=None, y_routes=None, out=None, stream=None):
+    """Stage one, stage two and the combine in one launch; counters (int32,
+    moe_a8w4_fused_counters entries) must be zero and are left zero.
+    Returns (inter_q, inter_s, y_routes, out)."""
+    dev = a_q.device
+    cap = moe_a8w4_sort_capacity(dims, block_m)
+    if inter_q is None:
+        inter_q = torch.empty((cap, dims.inter), dtype=torch.uint8, device=dev)
+    if inter_s is None:
+        inter_s = torch.empty((cap, dims.inter // 32), dtype=torch.uint8, device=dev)
+    if y_routes is None:
+        y_routes = torch.empty(route_rows_bytes(dims), dtype=torch.uint8, device=dev)
+    if out is None:
+        out = torch.empty((dims.tokens, dims.hidden), dtype=torch.bfloat16, device=dev)
+    st = load().moe_a8w4_stages_fused(ctypes.byref(dims), block_m, _ptr(a_q), _ptr(a_s), _ptr(sorted_ids),
+                                      _ptr(block_expert), _ptr(num_padded), _ptr(topk_ids),
+                                      _ptr(topk_weights), _ptr(w13_p), _ptr(w13_s_p), _ptr(w2_p),
+                                      _ptr(w2_s_p), _ptr(inter_q), _ptr(inter_s), _ptr(y_routes),
+                                      _ptr(counters), _ptr(out), _stream(stream))
+    _check("moe_a8w4_stages_fused", st)
+    return inter_q, inter_s, y_routes, out
 
 
 def moe_a8w4_combine(dims, topk_ids, y_routes, out=None, stream=None):

@@ -56,6 +56,17 @@ size_t route_rows_bytes(const moe_a8w4_dims* d) {
   return route_codes_bytes(d) + (size_t)d->tokens * d->topk * (d->hidden / 32);
 }
 
+// int32 counters of the fused decode launch: status word (in a 256-byte run
+// of its own), per-block stage-one counts (one 256-byte run each), per-block
+// stage-two counts, per (token, stage-two column range) route counts (at
+// most H/64 ranges).
+int64_t fused_counters(const moe_a8w4_dims* d, int bm) {
+  const int64_t blocks = capacity(d, bm) / bm;
+  return moe::kCounterStride * (1 + blocks) + blocks + (int64_t)d->tokens * (d->hidden / 64);
+}
+
+bool fused_bm(int bm) { return bm == 16 || bm == 32; }
+
 struct Layout {
   size_t aq, as, sorted, bexp, npad, iq, is, y, total;
 };
@@ -99,6 +110,21 @@ GemmArgs stage2_args(const moe_a8w4_dims* d, int bm, const uint8_t* iq, const ui
   a.y_codes = static_cast<int16_t*>(y);
   a.y_exps = static_cast<uint8_t*>(y) + route_codes_bytes(d);
   return a;
+}
+
+moe::FusedArgs fused_args(const moe_a8w4_dims* d, int bm, int32_t* cnt, const int32_t* topk_ids,
+                          void* out) {
+  moe::FusedArgs f = {};
+  const int64_t blocks = capacity(d, bm) / bm;
+  f.status = cnt;
+  f.block_done = cnt + moe::kCounterStride;
+  f.block_seen = cnt + moe::kCounterStride * (1 + blocks);
+  f.token_done = f.block_seen + blocks;
+  f.topk_ids = topk_ids;
+  f.num_experts = d->num_experts;
+  f.expert_offset = d->expert_offset;
+  f.out = static_cast<uint16_t*>(out);
+  return f;
 }
 
 }  // namespace
@@ -166,6 +192,8 @@ int forward_body(const moe_a8w4_dims* dims, const void* hidden, const int32_t* t
   uint8_t* y = ws + L.y;
   const int64_t max_blocks = capacity(dims, bm) / bm;
 
+  // four launches: at every decode size they measured faster than prep +
+  // moe_a8w4_stages_fused (the fused launch)
   hipError_t e = moe::launch_prep(topk_ids, dims->tokens, dims->topk, dims->num_experts,
                                   dims->expert_offset, bm, sorted, bexp, npad,
                                   static_cast<const uint16_t*>(hidden), dims->hidden, a_q, a_s, ra, stream);
@@ -290,7 +318,8 @@ int moe_a8w4_stage1(const moe_a8w4_dims* dims, int32_t block_m, const uint8_t* a
   const void* ptrs[9] = {a_q, a_s, sorted_ids, block_expert, num_padded, w13_p, w13_s_p, inter_q, inter_s};
   for (const void* p : ptrs)
     if (!p) return MOE_ERR_NULL;
-  if (!aligned(a_q, 16) || !aligned(w13_p, 16) || !aligned(w13_s_p, 16) || !aligned(inter_q, 16))
+  if (!aligned(a_q, 16) || !aligned(w13_p, 16) || !aligned(w13_s_p, 16) || !aligned(inter_q, 16) ||
+      !aligned(a_s, 4))
     return MOE_ERR_ALIGN;
   const int64_t max_blocks = capacity(dims, block_m) / block_m;
   return status_of(moe::launch_stage1(stage1_args(dims, block_m, a_q, a_s, sorted_ids, block_expert,
@@ -310,7 +339,8 @@ int moe_a8w4_stage2(const moe_a8w4_dims* dims, int32_t block_m, const uint8_t* i
                           w2_p, w2_s_p, y_routes, inter_q};
   for (const void* p : ptrs)
     if (!p) return MOE_ERR_NULL;
-  if (!aligned(inter_q, 16) || !aligned(w2_p, 16) || !aligned(w2_s_p, 16) || !aligned(y_routes, 16))
+  if (!aligned(inter_q, 16) || !aligned(w2_p, 16) || !aligned(w2_s_p, 16) || !aligned(y_routes, 16) ||
+      !aligned(inter_s, 4))
     return MOE_ERR_ALIGN;
   const int64_t max_blocks = capacity(dims, block_m) / block_m;
   return status_of(moe::launch_stage2(stage2_args(dims, block_m, inter_q, inter_s, sorted_ids,
@@ -331,6 +361,40 @@ int moe_a8w4_combine(const moe_a8w4_dims* dims, const int32_t* topk_ids, const v
                                        static_cast<const int16_t*>(y_routes),
                                        static_cast<const uint8_t*>(y_routes) + route_codes_bytes(dims),
                                        static_cast<uint16_t*>(out), stream));
+}
+
+int64_t moe_a8w4_fused_counters(const moe_a8w4_dims* dims, int32_t block_m) {
+  int st = check_dims(dims);
+  if (st) return st;
+  if (!fused_bm(block_m)) return MOE_ERR_BLOCK_M;
+  return fused_counters(dims, block_m);
+}
+
+int moe_a8w4_stages_fused(const moe_a8w4_dims* dims, int32_t block_m, const uint8_t* a_q,
+                          const uint8_t* a_s, const int32_t* sorted_ids, const int32_t* block_expert,
+                          const int32_t* num_padded, const int32_t* topk_ids, const float* topk_weights,
+                          const uint8_t* w13_p, const uint8_t* w13_s_p, const uint8_t* w2_p,
+                          const uint8_t* w2_s_p, uint8_t* inter_q, uint8_t* inter_s, void* y_routes,
+                          int32_t* counters, void* out, hipStream_t stream) {
+  int st = check_dims(dims);
+  if (st) return st;
+  if (!fused_bm(block_m)) return MOE_ERR_BLOCK_M;
+  if (dims->tokens == 0) return MOE_OK;
+  const void* ptrs[17] = {a_q, a_s, sorted_ids, block_expert, num_padded, topk_ids, topk_weights, w13_p,
+                          w13_s_p, w2_p, w2_s_p, inter_q, inter_s, y_routes, counters, out, a_q};
+  for (const void* p : ptrs)
+    if (!p) return MOE_ERR_NULL;
+  const void* al[8] = {a_q, w13_p, w13_s_p, w2_p, w2_s_p, inter_q, y_routes, out};
+  for (const void* p : al)
+    if (!aligned(p, 16)) return MOE_ERR_ALIGN;
+  if (!aligned(counters, 4) || !aligned(a_s, 4) || !aligned(inter_s, 4)) return MOE_ERR_ALIGN;
+  const int64_t max_blocks = capacity(dims, block_m) / block_m;
+  return status_of(moe::launch_fused(
+      stage1_args(dims, block_m, a_q, a_s, sorted_ids, block_expert, num_padded, w13_p, w13_s_p, inter_q,
+                  inter_s),
+      stage2_args(dims, block_m, inter_q, inter_s, sorted_ids, block_expert, num_padded, topk_weights,
+                  w2_p, w2_s_p, y_routes),
+      fused_args(dims, block_m, counters, topk_ids, out), max_blocks, stream));
 }
 
 const char* moe_a8w4_status_str(int status) {

@@ -64,6 +64,130 @@ __device__ __forceinline__ uint32_t f32_to_bf16(float f) {
   return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
 }
 
+// ----------------------------------------------- hand-over between workgroups
+//
+// Data one workgroup hands to another inside a launch (the fused decode
+// launch) goes through loads and stores that are coherent across the XCDs at
+// device scope with no cache maintenance: agent-scope relaxed atomics, which
+// gfx950 issues with the sc1 cache policy (written through to, and read back
+// from, the level all XCDs share).  Cache-wide release/acquire fences (L2
+// write-back and invalidate) cost far more when hundreds of workgroups use
+// them.  COH = false gives ordinary accesses.
+template <bool COH>
+__device__ __forceinline__ void st64(void* p, uint64_t v) {
+  if constexpr (COH) __hip_atomic_store(static_cast<uint64_t*>(p), v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  else *static_cast<uint64_t*>(p) = v;
+}
+template <bool COH>
+__device__ __forceinline__ void st16(void* p, uint16_t v) {
+  if constexpr (COH) __hip_atomic_store(static_cast<uint16_t*>(p), v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  else *static_cast<uint16_t*>(p) = v;
+}
+template <bool COH>
+__device__ __forceinline__ void st8(void* p, uint8_t v) {
+  if constexpr (COH) __hip_atomic_store(static_cast<uint8_t*>(p), v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  else *static_cast<uint8_t*>(p) = v;
+}
+template <bool COH>
+__device__ __forceinline__ void st128(void* p, v4i v) {
+  if constexpr (COH) {
+    st64<true>(p, (uint64_t)(uint32_t)v.x | ((uint64_t)(uint32_t)v.y << 32));
+    st64<true>(static_cast<uint8_t*>(p) + 8, (uint64_t)(uint32_t)v.z | ((uint64_t)(uint32_t)v.w << 32));
+  } else {
+    *static_cast<v4i*>(p) = v;
+  }
+}
+// The aligned 4 bytes holding byte p, with byte p at bit 8 (p & 3).  (A
+// coherent single-byte load would be zero-extended by an instruction right
+// behind it, which waits for every load in flight; the caller extracts the
+// byte where it is used instead.)
+template <bool COH>
+__device__ __forceinline__ uint32_t ld_word_of(const uint8_t* p) {
+  uint32_t* q = reinterpret_cast<uint32_t*>((uintptr_t)p & ~(uintptr_t)3);
+  if constexpr (COH) return __hip_atomic_load(q, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  else return *q;
+}
+__device__ __forceinline__ uint32_t byte_of(uint32_t word, const uint8_t* p) {
+  return (word >> (8 * ((uintptr_t)p & 3))) & 0xFFu;
+}
+// 16 bytes; NT: non-temporal when not coherent
+template <bool COH, bool NT = false>
+__device__ __forceinline__ v4i ld128(const void* p) {
+  if constexpr (COH) {
+    uint64_t* q = static_cast<uint64_t*>(const_cast<void*>(p));
+    const uint64_t lo = __hip_atomic_load(q, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const uint64_t hi = __hip_atomic_load(q + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    return v4i{(int)(uint32_t)lo, (int)(uint32_t)(lo >> 32), (int)(uint32_t)hi, (int)(uint32_t)(hi >> 32)};
+  } else if constexpr (NT) {
+    return __builtin_nontemporal_load(static_cast<const v4i*>(p));
+  } else {
+    return *static_cast<const v4i*>(p);
+  }
+}
+
+// Waits until every memory operation this wave has issued is complete (its
+// stores performed where ld/st with COH read them), before anything after it
+// is issued; the signal fences keep the compiler from moving memory accesses
+// across the wait.
+__device__ __forceinline__ void wait_memory() {
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __builtin_amdgcn_s_waitcnt(0);
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+}
+
+// Mask of a token's local slots: bit k set when topk_ids[t, k] names one of
+// the E experts held here (global ids expert_offset .. expert_offset + E - 1).
+__device__ __forceinline__ unsigned local_slots(const int32_t* ids, int64_t t, int topk, int E,
+                                                int expert_offset) {
+  unsigned mask = 0;
+#pragma unroll
+  for (int k = 0; k < kMaxTopk; ++k)
+    if (k < topk && (unsigned)(ids[t * topk + k] - expert_offset) < (unsigned)E) mask |= 1u << k;
+  return mask;
+}
+
+// Top-k combine of 8 consecutive outputs h .. h+7 of token t: BF16 (nearest
+// even) of the float32 sum, in ascending k over the slots in mask, of the
+// decoded route rows.  Each code decodes exactly (a 15-bit integer times a
+// power of two), so the sum does not depend on instruction selection; all of
+// the token's loads are issued before the first add.
+// COH: the route rows come from other workgroups of the same launch.
+template <bool COH = false>
+__device__ __forceinline__ void combine8(const int16_t* __restrict__ codes,
+                                         const uint8_t* __restrict__ exps, uint16_t* __restrict__ out,
+                                         int64_t t, int h, int H, int topk, unsigned mask) {
+  v4i c[kMaxTopk];
+  uint32_t sw[kMaxTopk];
+  const uint8_t* ex = exps + t * topk * (H / 32) + h / 32;
+#pragma unroll
+  for (int k = 0; k < kMaxTopk; ++k) {
+    if (mask & (1u << k)) {
+      c[k] = ld128<COH, true>(codes + (t * topk + k) * H + h);
+      sw[k] = ld_word_of<COH>(ex + k * (H / 32));
+    }
+  }
+  float a[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int k = 0; k < kMaxTopk; ++k) {
+    if (mask & (1u << k)) {
+      const float m = route_decode_mul((int)byte_of(sw[k], ex + k * (H / 32)));
+      const int w[4] = {c[k].x, c[k].y, c[k].z, c[k].w};
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        // code * 2^(S - 140) is exact, so the product rounds nothing
+        a[2 * j] += (float)(int16_t)(w[j] & 0xFFFF) * m;
+        a[2 * j + 1] += (float)(w[j] >> 16) * m;
+      }
+    }
+  }
+  uint4 r;
+  r.x = f32_to_bf16(a[0]) | (f32_to_bf16(a[1]) << 16);
+  r.y = f32_to_bf16(a[2]) | (f32_to_bf16(a[3]) << 16);
+  r.z = f32_to_bf16(a[4]) | (f32_to_bf16(a[5]) << 16);
+  r.w = f32_to_bf16(a[6]) | (f32_to_bf16(a[7]) << 16);
+  *reinterpret_cast<uint4*>(out + t * H + h) = r;
+}
+
 // Four scaled values to four E4M3 codes (element 0 lowest) with the gfx950
 // conversion instruction.  With the clamp to +-448 in front, its result is the
 // rule above (nearest, ties to even, saturating at 448, sign kept, subnormal

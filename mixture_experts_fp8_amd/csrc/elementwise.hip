@@ -15,8 +15,7 @@ namespace {
 // consecutive outputs; slots whose expert is not local were never written and
 // are skipped, so a token with no local route gets zeros.  The fixed
 // summation order makes the result bitwise repeatable.  H / 8 is a multiple of
-// 64, so the 64 lanes of a wave share one token: its slot mask is uniform, and
-// all of the token's slot loads are issued before the first add.
+// 64, so the 64 lanes of a wave share one token and its slot mask.
 __global__ void __launch_bounds__(256) combine_kernel(const int32_t* __restrict__ ids,
                                                       const int16_t* __restrict__ codes,
                                                       const uint8_t* __restrict__ exps,
@@ -27,40 +26,7 @@ __global__ void __launch_bounds__(256) combine_kernel(const int32_t* __restrict_
   for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n8; i += stride) {
     const int64_t t = __builtin_amdgcn_readfirstlane((int)(i / h8));
     const int h = (int)(i - t * h8) * 8;
-    unsigned mask = 0;
-#pragma unroll
-    for (int k = 0; k < kMaxTopk; ++k)
-      if (k < topk && (unsigned)(ids[t * topk + k] - expert_offset) < (unsigned)E) mask |= 1u << k;
-    v4i c[kMaxTopk];
-    int sx[kMaxTopk];
-#pragma unroll
-    for (int k = 0; k < kMaxTopk; ++k) {
-      if (mask & (1u << k)) {
-        const int64_t slot = t * topk + k;
-        c[k] = __builtin_nontemporal_load(reinterpret_cast<const v4i*>(codes + slot * H + h));
-        sx[k] = exps[slot * (H / 32) + h / 32];
-      }
-    }
-    float a[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int k = 0; k < kMaxTopk; ++k) {
-      if (mask & (1u << k)) {
-        const float m = route_decode_mul(sx[k]);
-        const int w[4] = {c[k].x, c[k].y, c[k].z, c[k].w};
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          // code * 2^(S - 140) is exact, so the product rounds nothing
-          a[2 * j] += (float)(int16_t)(w[j] & 0xFFFF) * m;
-          a[2 * j + 1] += (float)(w[j] >> 16) * m;
-        }
-      }
-    }
-    uint4 r;
-    r.x = f32_to_bf16(a[0]) | (f32_to_bf16(a[1]) << 16);
-    r.y = f32_to_bf16(a[2]) | (f32_to_bf16(a[3]) << 16);
-    r.z = f32_to_bf16(a[4]) | (f32_to_bf16(a[5]) << 16);
-    r.w = f32_to_bf16(a[6]) | (f32_to_bf16(a[7]) << 16);
-    *reinterpret_cast<uint4*>(out + t * H + h) = r;
+    combine8(codes, exps, out, t, h, H, topk, local_slots(ids, t, topk, E, expert_offset));
   }
 }
 

@@ -39,7 +39,8 @@ __device__ __forceinline__ int xcd_tile(int wg, int T) {
 // h = SiLU(gate) * up; the group's 32 columns form one per-1x32 quantisation
 // block, spread over the four lanes with equal t16.  Writes row p of the
 // intermediate (8 codes per lane, the scale from lane g = 0).  All 64 lanes
-// must call it together.
+// must call it together.  COH: another workgroup of the launch reads it.
+template <bool COH = false>
 __device__ __forceinline__ void stage1_store(const v4f acc[4], int64_t p, int grp, int I, int g,
                                              uint8_t* __restrict__ out_q, uint8_t* __restrict__ out_s) {
   float h[8];
@@ -58,8 +59,9 @@ __device__ __forceinline__ void stage1_store(const v4f acc[4], int64_t p, int gr
   amax = fmaxf(amax, __shfl_xor(amax, 16));
   amax = fmaxf(amax, __shfl_xor(amax, 32));
   const int E = block_exponent(amax);
-  *reinterpret_cast<uint2*>(out_q + p * I + grp * 32 + 8 * g) = encode8(h, exp2_neg(E));
-  if (g == 0) out_s[p * (I / 32) + grp] = (uint8_t)(E + 127);
+  const uint2 q = encode8(h, exp2_neg(E));
+  st64<COH>(out_q + p * I + grp * 32 + 8 * g, (uint64_t)q.x | ((uint64_t)q.y << 32));
+  if (g == 0) st8<COH>(out_s + p * (I / 32) + grp, (uint8_t)(E + 127));
 }
 
 // Route slot t * topk + k of a sorted id.
@@ -88,7 +90,8 @@ constexpr int kStage2Scratch = 16 * 144;
 // 0..31 in lanes g = 0, 1 and 32..63 in g = 2, 3).  The codes go through the
 // wave's LDS scratch so that each store instruction writes 8 routes x 128 B
 // in a row instead of 32-byte pieces of 16 routes.  All 64 lanes must call it
-// together.
+// together.  COH: another workgroup of the launch reads the rows.
+template <bool COH = false>
 __device__ __forceinline__ void stage2_store(const v4f acc[4], int64_t slot, float wt, const GemmArgs& args,
                                              int grp, int g, uint8_t* scr) {
   const int lane = threadIdx.x & 63, t16 = lane & 15;
@@ -121,10 +124,9 @@ __device__ __forceinline__ void stage2_store(const v4f acc[4], int64_t slot, flo
     const int route = 8 * q + (lane >> 3), chunk = lane & 7;
     const int64_t sl = ((int64_t)__shfl(shi, route) << 32) | (uint32_t)__shfl(slo, route);
     const v4i c = *reinterpret_cast<const v4i*>(scr + route * 144 + chunk * 16);
-    if (sl >= 0) *reinterpret_cast<v4i*>(args.y_codes + sl * args.N + grp * 64 + chunk * 8) = c;
+    if (sl >= 0) st128<COH>(args.y_codes + sl * args.N + grp * 64 + chunk * 8, c);
   }
-  if (g == 0 && slot >= 0)
-    *reinterpret_cast<uint16_t*>(args.y_exps + slot * (args.N / 32) + 2 * grp) = (uint16_t)(S | (S1 << 8));
+  if (g == 0 && slot >= 0) st16<COH>(args.y_exps + slot * (args.N / 32) + 2 * grp, (uint16_t)(S | (S1 << 8)));
   wave_lds_sync();
 }
 

@@ -27,6 +27,24 @@ struct GemmArgs {
   uint8_t* y_exps;        //          and their exponent bytes [M, topk, N/32]
 };
 
+// Cross-workgroup state of the fused decode launch (stage one, stage two and
+// the top-k combine in one kernel).  The counters are zero on entry and the
+// launch leaves them zero; status stays 0 unless a wait gave up.
+constexpr int kCounterStride = 64;   // int32 per block_done entry (one 256-byte run each)
+
+struct FusedArgs {
+  int32_t* block_done;    // [blocks * kCounterStride] stage-one tiles finished, per sorted block
+  int32_t* block_seen;    // [blocks] stage-two tiles past their wait, per block
+  int32_t* token_done;    // [M, stage-two tiles per block] routes finished per token and column range
+  int32_t* status;        // [1]
+  const int32_t* topk_ids;  // [M, topk] global expert ids
+  int32_t num_experts;    // E held here
+  int32_t expert_offset;  // global id of local expert 0
+  uint16_t* out;          // [M, H] BF16 output
+  int32_t ng1;            // stage-one tiles per block (set by the launcher)
+  int32_t g1, g2;         // workgroups of the stage-one and stage-two regions (set by the launcher)
+};
+
 // Router inputs and outputs (softmax top-k of the logits, optional shared slot).
 struct RouteArgs {
   const float* logits;    // [M, routed] router logits; null: the ids are given
@@ -54,6 +72,10 @@ hipError_t launch_pack(const uint8_t* src, const uint8_t* src_s, uint8_t* dst, u
 // max_blocks: upper bound of sorted blocks (grid size); kernels read the real count on device
 hipError_t launch_stage1(const GemmArgs& a, int64_t max_blocks, hipStream_t stream);
 hipError_t launch_stage2(const GemmArgs& a, int64_t max_blocks, hipStream_t stream);
+// Stage one (a1), stage two (a2) and the combine in one launch, bm = 16 or 32
+// (gemm.hip); the counters of fa must be zero
+hipError_t launch_fused(const GemmArgs& a1, const GemmArgs& a2, const FusedArgs& fa, int64_t max_blocks,
+                        hipStream_t stream);
 // LDS-tiled variant of either stage for bm = 64 or 128 (gemm_tile.hip)
 hipError_t launch_tile(int stage, const GemmArgs& a, int64_t max_blocks, hipStream_t stream);
 
