@@ -81,6 +81,11 @@ def _load():
     lib.oracle_forward_given_intermediate.argtypes = ([c_i64, c_i64, c_i64, c_int, c_int, c_int]
                                                       + [vp] * 4 + [vp, c_i64, vp, vp, vp, vp])
     lib.oracle_forward_given_intermediate.restype = None
+    lib.oracle_a16_stage1.argtypes = [c_i64, c_i64, vp, vp, vp, vp, vp]
+    lib.oracle_a16_stage1.restype = None
+    lib.oracle_a16_forward.argtypes = ([c_i64, c_i64, c_i64, c_int, c_int, c_int] + [vp] * 7
+                                       + [vp, c_i64, vp, vp, vp])
+    lib.oracle_a16_forward.restype = None
     lib.oracle_softmax_topk.argtypes = [c_i64, c_int, c_int, c_int, vp, vp, vp]
     lib.oracle_softmax_topk.restype = None
     lib.oracle_num_threads.argtypes = []
@@ -211,6 +216,49 @@ def forward(hidden_bf16, topk_ids, topk_weights, w13, w13_s, w2, w2_s,
                            _p(w13), _p(w13_s), _p(w2), _p(w2_s),
                            _p(tok), ntok, _p(o64), _p(out))
     return (out, o64) if want_f64 else out
+
+
+def a16_stage1(x_bf16_row, w13_e, w13_s_e):
+    """A16W4 stage one for one route -> (h FP64 [I], BF16 bits [I])."""
+    x = _c(x_bf16_row, np.uint16)
+    w13_e = _c(w13_e, np.uint8)
+    w13_s_e = _c(w13_s_e, np.uint8)
+    H = x.shape[0]
+    I = w13_e.shape[0] // 2
+    h = np.zeros(I, np.float64)
+    hb = np.zeros(I, np.uint16)
+    _load().oracle_a16_stage1(H, I, _p(x), _p(w13_e), _p(w13_s_e), _p(h), _p(hb))
+    return h, hb
+
+
+def a16_forward(hidden_bf16, topk_ids, topk_weights, w13, w13_s, w2, w2_s,
+                expert_offset: int = 0, tokens=None, want_f64: bool = False,
+                want_inter: bool = False):
+    """The A16W4 layer's BF16 output (uint16 bits) for all tokens or a list of
+    tokens; optionally the FP64 combine and the BF16 intermediate
+    [ntok, topk, I] (zero for non-local slots)."""
+    x = _c(hidden_bf16, np.uint16)
+    ids = _c(topk_ids, np.int32)
+    wts = _c(topk_weights, np.float32)
+    w13, w13_s, w2, w2_s = (_c(a, np.uint8) for a in (w13, w13_s, w2, w2_s))
+    M, H = x.shape
+    k = ids.shape[1]
+    E = w13.shape[0]
+    I = w13.shape[1] // 2
+    tok = None if tokens is None else _c(tokens, np.int64)
+    ntok = M if tokens is None else tok.shape[0]
+    out = np.zeros((ntok, H), np.uint16)
+    o64 = np.zeros((ntok, H), np.float64) if want_f64 else None
+    inter = np.zeros((ntok, k, I), np.uint16) if want_inter else None
+    _load().oracle_a16_forward(M, H, I, E, expert_offset, k, _p(x), _p(ids), _p(wts),
+                               _p(w13), _p(w13_s), _p(w2), _p(w2_s), _p(tok), ntok,
+                               _p(inter), _p(o64), _p(out))
+    res = (out,)
+    if want_f64:
+        res += (o64,)
+    if want_inter:
+        res += (inter,)
+    return res if len(res) > 1 else out
 
 
 def intermediate(hidden_bf16, topk_ids, w13, w13_s, routes, expert_offset: int = 0,

@@ -1,5 +1,6 @@
 /*
- * moe_oracle.c -- CPU oracle for the A8W4 fused mixture-of-experts layer.
+ * moe_oracle.c -- CPU oracle for the A8W4 fused mixture-of-experts layer
+ * (and its A16W4 variant, further down).
  *
  * TEST INFRASTRUCTURE ONLY.  This file is the slow, plain, FP64 statement of
  * what the layer computes.  Only the tests, the smoke check and the CPU
@@ -401,6 +402,89 @@ void oracle_forward_given_intermediate(int64_t M, int64_t H, int64_t I, int E, i
         if (le < 0 || le >= E) continue;
         oracle_stage2(H, I, inter_q + r * I, inter_s + r * (I / 32),
                       w2 + le * H * (I / 2), w2_s + le * H * (I / 32), y + r * H);
+    }
+    combine(H, E, expert_offset, topk, topk_ids, topk_weights, tokens, ntok, y, out_f64, out_bf16);
+    free(y);
+}
+
+/* ------------------------------------------------- A16W4 variant (one route) */
+
+/* The A16W4 variant of the layer (aiter PR 6286, "Retune gfx942 a16w4
+ * DSv4.1 tiles for Triton 3.8": moe_gemm_a16w4 with w1 under apply_swiglu,
+ * w2 separate, BF16 activations, MXFP4 weights).  Readings taken where that
+ * page is silent: the activations enter unquantised (their exact BF16
+ * values); w13/w2 layout, interleave, nibble order and the SwiGLU are those
+ * of the A8W4 layer above (SiLU(g) * u, no clamp); the intermediate between
+ * the two GEMMs is BF16 (nearest, ties to even) -- the 16-bit activation
+ * type of the second GEMM; the routing weight multiplies the stage-two
+ * result and the top-k sum is the A8W4 combine.
+ *
+ * Stage one for one route: h_j = BF16(SiLU(g_j) * u_j) with g_j, u_j the FP64
+ * dot products of the token's BF16 row with rows 2j and 2j+1 of w13[e].
+ *   x    the token's BF16 row (H values)
+ *   h64  out, I values of SiLU(g) * u before the rounding (may be NULL)
+ *   hb   out, I BF16 values of the intermediate */
+void oracle_a16_stage1(int64_t H, int64_t I, const uint16_t* x,
+                       const uint8_t* w13, const uint8_t* w13_s, double* h64, uint16_t* hb)
+{
+    e4m3_table_init();
+    double* a = (double*)malloc(sizeof(double) * H);
+    for (int64_t kk = 0; kk < H; ++kk) a[kk] = oracle_bf16_value(x[kk]);
+    for (int64_t j = 0; j < I; ++j) {
+        double g = 0.0, u = 0.0;
+        for (int64_t kk = 0; kk < H; ++kk) {
+            g += a[kk] * mxfp4_elem(w13, w13_s, H, 2 * j, kk);
+            u += a[kk] * mxfp4_elem(w13, w13_s, H, 2 * j + 1, kk);
+        }
+        double h = g / (1.0 + exp(-g)) * u;
+        if (h64) h64[j] = h;
+        hb[j] = oracle_bf16_rne(h);
+    }
+    free(a);
+}
+
+/* Stage two for one route of the A16W4 variant: y_h = sum_j h_j * w2[e][h, j]
+ * in FP64 over the BF16 intermediate h. */
+void oracle_a16_stage2(int64_t H, int64_t I, const uint16_t* hb,
+                       const uint8_t* w2, const uint8_t* w2_s, double* y)
+{
+    e4m3_table_init();
+    double* hv = (double*)malloc(sizeof(double) * I);
+    for (int64_t j = 0; j < I; ++j) hv[j] = oracle_bf16_value(hb[j]);
+    for (int64_t hh = 0; hh < H; ++hh) {
+        double acc = 0.0;
+        for (int64_t j = 0; j < I; ++j) acc += hv[j] * mxfp4_elem(w2, w2_s, I, hh, j);
+        y[hh] = acc;
+    }
+    free(hv);
+}
+
+/* The A16W4 layer's output for a list of tokens (arguments as
+ * oracle_forward); inter_bf16, if not NULL, receives the BF16 intermediate
+ * [ntok, topk, I] of the listed tokens' local slots (others left as given). */
+void oracle_a16_forward(int64_t M, int64_t H, int64_t I, int E, int expert_offset, int topk,
+                        const uint16_t* hidden, const int32_t* topk_ids, const float* topk_weights,
+                        const uint8_t* w13, const uint8_t* w13_s,
+                        const uint8_t* w2, const uint8_t* w2_s,
+                        const int64_t* tokens, int64_t ntok,
+                        uint16_t* inter_bf16, double* out_f64, uint16_t* out_bf16)
+{
+    e4m3_table_init();
+    if (!tokens) ntok = M;
+    int64_t nroute = ntok * topk;
+    double* y = (double*)calloc((size_t)(nroute > 0 ? nroute : 1) * H, sizeof(double));
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t r = 0; r < nroute; ++r) {
+        int64_t i = r / topk, k = r % topk;
+        int64_t t = tokens ? tokens[i] : i;
+        int64_t le = (int64_t)topk_ids[t * topk + k] - expert_offset;
+        if (le < 0 || le >= E) continue;
+        uint16_t* hb = (uint16_t*)malloc(sizeof(uint16_t) * I);
+        oracle_a16_stage1(H, I, hidden + t * H, w13 + le * (2 * I) * (H / 2),
+                          w13_s + le * (2 * I) * (H / 32), NULL, hb);
+        if (inter_bf16) memcpy(inter_bf16 + r * I, hb, sizeof(uint16_t) * I);
+        oracle_a16_stage2(H, I, hb, w2 + le * H * (I / 2), w2_s + le * H * (I / 32), y + r * H);
+        free(hb);
     }
     combine(H, E, expert_offset, topk, topk_ids, topk_weights, tokens, ntok, y, out_f64, out_bf16);
     free(y);

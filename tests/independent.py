@@ -160,3 +160,49 @@ def bf16_round_bruteforce(x):
                 best = (key, cand)
         res[i] = best[1] | (0x8000 if math.copysign(1.0, xv) < 0 else 0)
     return res
+
+
+def _int_parts_bf16(bits):
+    """BF16 bits -> (n, p) with value = n * 2^p exactly (finite values)."""
+    b = np.asarray(bits, np.uint16).astype(np.int64)
+    e = (b >> 7) & 0xFF
+    m = b & 0x7F
+    n = np.where(e == 0, m, m + 128)
+    p = np.where(e == 0, -133, e - 134)
+    return np.where(b & 0x8000, -n, n), p
+
+
+def bruteforce_a16_forward(hidden_bits, topk_ids, topk_weights, w13, w13_s, w2, w2_s, expert_offset=0):
+    """The A16W4 variant route by route: exact dot products of the BF16
+    activations with the MXFP4 rows, SiLU(g) * u rounded to BF16 by the
+    brute-force neighbour search, exact stage-two dot products, exact sum of
+    the weighted routes.  Returns (o as float64 [M, H], {f: BF16 bits [I]})."""
+    M, H = hidden_bits.shape
+    E = w13.shape[0]
+    I = w13.shape[1] // 2
+    k = topk_ids.shape[1]
+    out = np.zeros((M, H), np.float64)
+    inter = {}
+    for t in range(M):
+        na, pa = _int_parts_bf16(hidden_bits[t])
+        o = [Fraction(0)] * H
+        for s in range(k):
+            e = int(topk_ids[t, s]) - expert_offset
+            if e < 0 or e >= E:
+                continue
+            h = np.zeros(I)
+            for j in range(I):
+                ng, pg = _int_parts_fp4(w13[e, 2 * j], w13_s[e, 2 * j])
+                nu, pu = _int_parts_fp4(w13[e, 2 * j + 1], w13_s[e, 2 * j + 1])
+                g = float(exact_dot(na, pa, ng, pg))
+                u = float(exact_dot(na, pa, nu, pu))
+                h[j] = g / (1.0 + math.exp(-g)) * u
+            hb = bf16_round_bruteforce(h)
+            inter[t * k + s] = hb
+            nh, ph = _int_parts_bf16(hb)
+            wk = Fraction(float(topk_weights[t, s]))
+            for hh in range(H):
+                n2, p2 = _int_parts_fp4(w2[e, hh], w2_s[e, hh])
+                o[hh] += wk * exact_dot(nh, ph, n2, p2)
+        out[t] = [float(v) for v in o]
+    return out, inter

@@ -1,0 +1,68 @@
+"""Pins of the oracle's A16W4 variant (BF16 activations x MXFP4 weights, w1
+with fused SwiGLU, BF16 intermediate, w2 separate; aiter PR 6286, "Retune
+gfx942 a16w4 DSv4.1 tiles for Triton 3.8"): a dense numpy SwiGLU MLP for a
+single expert, exact integer brute force on tiny shapes, and invariants."""
+import numpy as np
+import pytest
+
+from mixture_experts_fp8_amd import workloads as wl
+import independent as ind
+
+
+def small(H=256, I=64, E=8, topk=3, cid=190):
+    return wl.Workload("small-a16", H, I, I, E, E, topk, False, 0, (), ("softmax",), cid)
+
+
+@pytest.mark.parametrize("H,I,M", [(256, 64, 5), (512, 128, 3), (5120, 768, 2)])
+def test_a16_single_expert_top1_equals_dense_swiglu(oracle, H, I, M):
+    w = small(H=H, I=I, E=1, topk=1, cid=191)
+    w13, w13_s, w2, w2_s = wl.make_weights(w)
+    hidden = wl.make_hidden(np.random.default_rng(8), M, H)
+    ids = np.zeros((M, 1), np.int32)
+    wts = np.ones((M, 1), np.float32)
+    out, o64, inter = oracle.a16_forward(hidden, ids, wts, w13, w13_s, w2, w2_s, want_f64=True,
+                                         want_inter=True)
+    X = ind.bf16_to_f64(hidden)
+    W13 = ind.dequant_mxfp4(w13[0], w13_s[0])
+    g = X @ W13[0::2].T
+    u = X @ W13[1::2].T
+    hb = ind.bf16_round_bruteforce((g / (1.0 + np.exp(-g)) * u).ravel()).reshape(M, I)
+    assert np.array_equal(inter[:, 0], hb)
+    y = ind.bf16_to_f64(hb) @ ind.dequant_mxfp4(w2[0], w2_s[0]).T
+    np.testing.assert_allclose(o64, y, rtol=1e-12, atol=1e-12 * np.abs(y).max())
+    assert np.array_equal(out[0, :1000], ind.bf16_round_bruteforce(y[0, :1000]))
+
+
+@pytest.mark.parametrize("case", [
+    dict(H=64, I=64, E=4, topk=2, M=5, mode="softmax"),
+    dict(H=128, I=128, E=3, topk=3, M=3, mode="roundrobin"),
+])
+def test_a16_oracle_equals_exact_bruteforce(oracle, case):
+    w = small(H=case["H"], I=case["I"], E=case["E"], topk=case["topk"], cid=192)
+    w13, w13_s, w2, w2_s = wl.make_weights(w)
+    hidden, ids, wts = wl.make_inputs(w, case["M"], case["mode"], seed=[192, case["M"]])
+    ids = ids.copy()
+    ids[0, 0] = -1                       # a non-local slot is skipped
+    out, o64, inter = oracle.a16_forward(hidden, ids, wts, w13, w13_s, w2, w2_s, want_f64=True,
+                                         want_inter=True)
+    ref, rinter = ind.bruteforce_a16_forward(hidden, ids, wts, w13, w13_s, w2, w2_s)
+    np.testing.assert_allclose(o64, ref, rtol=1e-12, atol=1e-12 * np.abs(ref).max())
+    for f, hb in rinter.items():
+        assert np.array_equal(inter[f // case["topk"], f % case["topk"]], hb)
+    assert np.array_equal(out.ravel(), ind.bf16_round_bruteforce(ref.ravel()))
+
+
+def test_a16_invariants(oracle):
+    w = small(H=256, I=64, E=8, topk=3, cid=193)
+    w13, w13_s, w2, w2_s = wl.make_weights(w)
+    hidden, ids, wts = wl.make_inputs(w, 6, "softmax", seed=[193])
+    _, o1 = oracle.a16_forward(hidden, ids, wts, w13, w13_s, w2, w2_s, want_f64=True)
+    _, o2 = oracle.a16_forward(hidden, ids, wts * 2, w13, w13_s, w2, w2_s, want_f64=True)
+    assert np.array_equal(o2, 2 * o1)            # the routing weight multiplies stage two
+    perm = [2, 0, 1]
+    _, o3 = oracle.a16_forward(hidden, ids[:, perm], wts[:, perm], w13, w13_s, w2, w2_s, want_f64=True)
+    np.testing.assert_allclose(o3, o1, rtol=1e-13, atol=1e-13 * np.abs(o1).max())
+    # the listed-token form gives the same rows
+    sub = np.array([5, 0, 3], np.int64)
+    full = oracle.a16_forward(hidden, ids, wts, w13, w13_s, w2, w2_s)
+    assert np.array_equal(oracle.a16_forward(hidden, ids, wts, w13, w13_s, w2, w2_s, tokens=sub), full[sub])
