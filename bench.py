@@ -36,6 +36,7 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBS = 8000.0           # MI355X HBM3E, GB/s
 FP8_PEAK_TFLOPS = 5000.0        # dense MFMA, FP8 operands (the A operand here is FP8)
 FP4_PEAK_TFLOPS = 10100.0       # dense MFMA, FP4/FP6 operands
+BF16_PEAK_TFLOPS = 2500.0       # dense MFMA, BF16 operands (the A16W4 variant)
 BUCKETS = (6, 12, 24, 48, 96, 192, 384, 768)
 # A short spin kernel in front of a single timed call keeps host-side launch
 # latency out of its event interval (about 100 us of GPU clock).
@@ -62,6 +63,8 @@ def parse():
     ap.add_argument("--fused-table", action="store_true",
                     help="instead of the decode sweep: per decode bucket, the layer as four launches "
                          "against the fused decode launch")
+    ap.add_argument("--a16w4-table", action="store_true",
+                    help="instead of the decode sweep: the A16W4 variant at the pages' A16W4 sizes")
     ap.add_argument("--router-table", action="store_true",
                     help="instead of the decode sweep: per backbone decode bucket, the router alone, "
                          "the layer from given routes and the layer from router logits (JSON line)")
@@ -229,6 +232,67 @@ def fused_table(args):
                       "rows": rows}))
 
 
+# The pages' isolated A16W4 w1 + w2 times on MI325X (gfx942, Triton 3.8), this
+# PR's column, microseconds (aiter PR 6286, the author's reply table; rows
+# whose w1 was left out there have no sum).  Another chip: context only.
+PAGES_A16W4_US = {
+    "a16w4-backbone": {12: 138.7 + 69.3, 256: 614.9 + 304.4, 1024: 606.5 + 310.2, 1536: 722.4 + 457.0,
+                       4096: 1178.5 + 584.1, 16384: None},
+    "a16w4-shared": {12: 168.3 + 82.5, 256: 608.7 + 304.1, 1024: 725.4 + 461.6, 1536: 714.0 + 437.5,
+                     4096: None, 16384: None},
+}
+
+
+def a16w4_table(args):
+    """Median microseconds per moe_a16w4_forward call (the A16W4 variant: BF16
+    activations x MXFP4 weights) at the pages' A16W4 sizes, round-robin
+    routing, with algorithmic GB/s and TFLOP/s (bf16 MFMA peak 2.5 PFLOP/s)."""
+    import torch
+    from mixture_experts_fp8_amd import abi, workloads as wl
+    dev = torch.device("cuda:0")
+    tables = {}
+    for name in ("a16w4-backbone", "a16w4-shared"):
+        w = wl.WORKLOADS[name]
+        host_w = wl.make_weights(w)
+        d1 = abi.make_dims(1, w.hidden, w.inter, w.num_experts, w.topk)
+        raw = [torch.from_numpy(np.ascontiguousarray(x)).to(dev) for x in host_w]
+        packed = abi.moe_a8w4_pack_weights(d1, *raw)
+        del raw, host_w
+        rows = {}
+        for M in w.tokens:
+            hidden, ids, wts = wl.make_inputs(w, M, "roundrobin")
+            d = abi.make_dims(M, w.hidden, w.inter, w.num_experts, w.topk, w.expert_offset, w.routed_experts)
+            x = torch.from_numpy(hidden.view(np.int16)).to(dev).view(torch.bfloat16)
+            idd = torch.from_numpy(ids).to(dev)
+            wd = torch.from_numpy(wts).to(dev)
+            out = torch.empty((M, w.hidden), dtype=torch.bfloat16, device=dev)
+            ws = torch.empty(abi.moe_a16w4_workspace_bytes(d), dtype=torch.uint8, device=dev)
+            fwd = lambda: abi.moe_a16w4_forward(d, x, idd, wd, *packed, out=out, workspace=ws)
+            for _ in range(args.warmup):
+                fwd()
+            torch.cuda.synchronize()
+            us = _timed_us(fwd, args.steps)
+            a = algorithmic(w, M, ids)
+            # BF16 activations: 2 bytes per element read by stage one, BF16 intermediate
+            nbytes = a["bytes"] - 2 * M * (w.hidden + w.hidden // 32) + M * w.hidden * 2 \
+                - 2 * a["R"] * (w.inter + w.inter // 32) + 2 * a["R"] * w.inter * 2
+            pages = PAGES_A16W4_US[name][M]
+            rows[str(M)] = dict(us_per_call=round(us, 1), routes=a["R"], experts_touched=a["D"],
+                                block_m=abi.moe_a16w4_block_m(d), GBps=round(nbytes / us / 1e3, 1),
+                                hbm_frac=round(nbytes / us / 1e3 / HBM_PEAK_GBS, 3),
+                                TFLOPs=round(a["flops"] / us / 1e6, 1),
+                                mfma_frac_bf16=round(a["flops"] / us / 1e6 / BF16_PEAK_TFLOPS, 4),
+                                pages_mi325x_w1_w2_us=None if pages is None else round(pages, 1))
+            print("%s M=%5d  %s" % (name, M, rows[str(M)]), file=sys.stderr, flush=True)
+        tables[name] = rows
+        del packed
+        torch.cuda.empty_cache()
+    print(json.dumps({"table": "A16W4 variant (BF16 activations x MXFP4), one MI355X", "unit": "us/call",
+                      "config": {"workload": "H5120, w1 N1536 K5120, w2 N5120 K768; 384 experts top-6 and "
+                                             "385 top-7 with the shared expert; round-robin routing"},
+                      "tables": tables}))
+
+
 def router_table(args):
     """Backbone decode buckets: microseconds of the router alone, of the layer
     from given routes (moe_a8w4_forward) and from router logits
@@ -325,6 +389,9 @@ def main():
         return
     if args.fused_table:
         fused_table(args)
+        return
+    if args.a16w4_table:
+        a16w4_table(args)
         return
     if args.profile_call:
         profile_call(args)

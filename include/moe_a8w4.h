@@ -232,6 +232,40 @@ int moe_a8w4_stages_fused(const moe_a8w4_dims* dims, int32_t block_m, const uint
  * invalid dims, or block_m other than 16 and 32). */
 int64_t moe_a8w4_fused_counters(const moe_a8w4_dims* dims, int32_t block_m);
 
+/* ------------------------------------------------------ the A16W4 variant */
+
+/* The A16W4 variant of the layer (aiter PR 6286, "Retune gfx942 a16w4 DSv4.1
+ * tiles for Triton 3.8": w1 with the SwiGLU fused, w2 separate, BF16
+ * activations, MXFP4 weights).  The same dims, weights packed by
+ * moe_a8w4_pack_weights and routing as moe_a8w4_forward; the activations
+ * are not quantised: stage one multiplies the BF16 hidden rows by the
+ * dequantised w13 (FP32 accumulation), the intermediate SiLU(gate) * up is
+ * rounded to BF16 (nearest, ties to even), stage two multiplies it by w2,
+ * and the routing-weighted routes are combined as in moe_a8w4_forward.
+ * Blocks of 16 or 32 routes (moe_a16w4_block_m); the weights are exact in
+ * BF16 for every scale code whose products stay normal (codes 1 ... 254
+ * with |element| >= 0.5 scaled above 2^-126).  Four launches: sort, stage
+ * one, stage two, combine.  Errors, ownership and stream rules as
+ * moe_a8w4_forward. */
+int moe_a16w4_forward(const moe_a8w4_dims* dims, const void* hidden, const int32_t* topk_ids,
+                      const float* topk_weights, const uint8_t* w13_p, const uint8_t* w13_s_p,
+                      const uint8_t* w2_p, const uint8_t* w2_s_p, void* out, void* workspace,
+                      size_t workspace_bytes, hipStream_t stream);
+
+/* Bytes of workspace moe_a16w4_forward needs for these dims. */
+int moe_a16w4_workspace_bytes(const moe_a8w4_dims* dims, size_t* bytes);
+
+/* Rows per sorted block (16 or 32) that moe_a16w4_forward uses. */
+int moe_a16w4_block_m(const moe_a8w4_dims* dims);
+
+/* Stage one of the A16W4 variant for every sorted block (sort buffers from
+ * moe_a8w4_sort with this block_m, 16 or 32): inter_bf16 [capacity, I] BF16,
+ * row p = sorted position, holding BF16(SiLU(gate) * up); rows of blocks
+ * that hold a route are written in full. */
+int moe_a16w4_stage1(const moe_a8w4_dims* dims, int32_t block_m, const void* hidden,
+                     const int32_t* sorted_ids, const int32_t* block_expert, const int32_t* num_padded,
+                     const uint8_t* w13_p, const uint8_t* w13_s_p, void* inter_bf16, hipStream_t stream);
+
 /* Name of a status code (static string). */
 const char* moe_a8w4_status_str(int status);
 

@@ -29,6 +29,7 @@ EXPORTS = (
     "moe_a8w4_quant_sort",
     "moe_a8w4_stage1", "moe_a8w4_stage2", "moe_a8w4_combine", "moe_a8w4_status_str",
     "moe_a8w4_route", "moe_a8w4_forward_routed", "moe_a8w4_stages_fused", "moe_a8w4_fused_counters",
+    "moe_a16w4_forward", "moe_a16w4_workspace_bytes", "moe_a16w4_block_m", "moe_a16w4_stage1",
 )
 
 
@@ -78,6 +79,10 @@ def load() -> ctypes.CDLL:
         "moe_a8w4_forward_routed": (ctypes.c_int, [P, vp, vp, i32] + [vp] * 8 + [sz, vp]),
         "moe_a8w4_stages_fused": (ctypes.c_int, [P, i32] + [vp] * 16 + [vp]),
         "moe_a8w4_fused_counters": (ctypes.c_int64, [P, i32]),
+        "moe_a16w4_forward": (ctypes.c_int, [P] + [vp] * 9 + [sz, vp]),
+        "moe_a16w4_workspace_bytes": (ctypes.c_int, [P, ctypes.POINTER(sz)]),
+        "moe_a16w4_block_m": (ctypes.c_int, [P]),
+        "moe_a16w4_stage1": (ctypes.c_int, [P, i32] + [vp] * 7 + [vp]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -300,6 +305,47 @@ def moe_a8w4_stages_fused(dims, block_m, a_q, a_s, sorted_ids, block_expert, num
                                       _ptr(counters), _ptr(out), _stream(stream))
     _check("moe_a8w4_stages_fused", st)
     return inter_q, inter_s, y_routes, out
+
+
+def moe_a16w4_workspace_bytes(dims) -> int:
+    n = ctypes.c_size_t()
+    _check("moe_a16w4_workspace_bytes", load().moe_a16w4_workspace_bytes(ctypes.byref(dims), ctypes.byref(n)))
+    return n.value
+
+
+def moe_a16w4_block_m(dims) -> int:
+    bm = load().moe_a16w4_block_m(ctypes.byref(dims))
+    if bm < 0:
+        raise MoeError("moe_a16w4_block_m", bm)
+    return bm
+
+
+def moe_a16w4_forward(dims, hidden, topk_ids, topk_weights, w13_p, w13_s_p, w2_p, w2_s_p,
+                      out=None, workspace=None, stream=None):
+    """The A16W4 variant of the layer: BF16 hidden [M, H] -> BF16 out [M, H]."""
+    dev = hidden.device
+    if out is None:
+        out = torch.empty((dims.tokens, dims.hidden), dtype=torch.bfloat16, device=dev)
+    if workspace is None:
+        workspace = torch.empty(max(moe_a16w4_workspace_bytes(dims), 1), dtype=torch.uint8, device=dev)
+    st = load().moe_a16w4_forward(ctypes.byref(dims), _ptr(hidden), _ptr(topk_ids), _ptr(topk_weights),
+                                  _ptr(w13_p), _ptr(w13_s_p), _ptr(w2_p), _ptr(w2_s_p), _ptr(out),
+                                  _ptr(workspace), workspace.numel(), _stream(stream))
+    _check("moe_a16w4_forward", st)
+    return out
+
+
+def moe_a16w4_stage1(dims, block_m, hidden, sorted_ids, block_expert, num_padded, w13_p, w13_s_p,
+                     inter=None, stream=None):
+    """A16W4 stage one -> BF16 intermediate [capacity, I] in sorted-row order."""
+    if inter is None:
+        cap = moe_a8w4_sort_capacity(dims, block_m)
+        inter = torch.empty((cap, dims.inter), dtype=torch.bfloat16, device=hidden.device)
+    st = load().moe_a16w4_stage1(ctypes.byref(dims), block_m, _ptr(hidden), _ptr(sorted_ids),
+                                 _ptr(block_expert), _ptr(num_padded), _ptr(w13_p), _ptr(w13_s_p),
+                                 _ptr(inter), _stream(stream))
+    _check("moe_a16w4_stage1", st)
+    return inter
 
 
 def moe_a8w4_combine(dims, topk_ids, y_routes, out=None, stream=None):

@@ -127,6 +127,42 @@ moe::FusedArgs fused_args(const moe_a8w4_dims* d, int bm, int32_t* cnt, const in
   return f;
 }
 
+// A16W4 variant: blocks of 16 routes while an expert averages at most 8,
+// else 32 (its decode-class kernel keeps a block's tokens in registers).
+int a16_bm(const moe_a8w4_dims* d) {
+  const int experts = d->routed_experts > d->num_experts ? d->routed_experts : d->num_experts;
+  return (double)d->tokens * d->topk / experts <= 8.0 ? 16 : 32;
+}
+
+struct A16Layout {
+  size_t sorted, bexp, npad, inter, y, total;
+};
+
+// sort buffers, BF16 intermediate [capacity, I], route rows
+A16Layout a16_layout(const moe_a8w4_dims* d, int bm) {
+  const size_t cap = (size_t)capacity(d, bm);
+  A16Layout L;
+  size_t o = 0;
+  L.sorted = o; o += al256(cap * 4);
+  L.bexp = o;   o += al256(cap / bm * 4);
+  L.npad = o;   o += 256;
+  L.inter = o;  o += al256(cap * d->inter * 2);
+  L.y = o;      o += al256(route_rows_bytes(d));
+  L.total = o;
+  return L;
+}
+
+GemmArgs a16_stage1_args(const moe_a8w4_dims* d, int bm, const void* hidden, const int32_t* sorted,
+                         const int32_t* bexp, const int32_t* npad, const uint8_t* w, const uint8_t* ws,
+                         void* inter) {
+  GemmArgs a = {};
+  a.M = d->tokens; a.topk = d->topk; a.N = 2 * d->inter; a.K = d->hidden; a.bm = bm;
+  a.sorted_ids = sorted; a.block_expert = bexp; a.num_padded = npad;
+  a.bq = static_cast<const uint8_t*>(hidden); a.w = w; a.ws = ws;
+  a.out_q = static_cast<uint8_t*>(inter);
+  return a;
+}
+
 }  // namespace
 
 extern "C" {
@@ -395,6 +431,79 @@ int moe_a8w4_stages_fused(const moe_a8w4_dims* dims, int32_t block_m, const uint
       stage2_args(dims, block_m, inter_q, inter_s, sorted_ids, block_expert, num_padded, topk_weights,
                   w2_p, w2_s_p, y_routes),
       fused_args(dims, block_m, counters, topk_ids, out), max_blocks, stream));
+}
+
+// ------------------------------------------------------- A16W4 variant
+
+int moe_a16w4_block_m(const moe_a8w4_dims* dims) {
+  int st = check_dims(dims);
+  if (st) return st;
+  return a16_bm(dims);
+}
+
+int moe_a16w4_workspace_bytes(const moe_a8w4_dims* dims, size_t* bytes) {
+  int st = check_dims(dims);
+  if (st) return st;
+  if (!bytes) return MOE_ERR_NULL;
+  *bytes = a16_layout(dims, a16_bm(dims)).total;
+  return MOE_OK;
+}
+
+int moe_a16w4_stage1(const moe_a8w4_dims* dims, int32_t block_m, const void* hidden,
+                     const int32_t* sorted_ids, const int32_t* block_expert, const int32_t* num_padded,
+                     const uint8_t* w13_p, const uint8_t* w13_s_p, void* inter_bf16, hipStream_t stream) {
+  int st = check_dims(dims);
+  if (st) return st;
+  if (block_m != 16 && block_m != 32) return MOE_ERR_BLOCK_M;
+  if (dims->tokens == 0) return MOE_OK;
+  const void* ptrs[7] = {hidden, sorted_ids, block_expert, num_padded, w13_p, w13_s_p, inter_bf16};
+  for (const void* p : ptrs)
+    if (!p) return MOE_ERR_NULL;
+  if (!aligned(hidden, 16) || !aligned(w13_p, 16) || !aligned(w13_s_p, 16) || !aligned(inter_bf16, 16))
+    return MOE_ERR_ALIGN;
+  return status_of(moe::launch_a16_stage1(
+      a16_stage1_args(dims, block_m, hidden, sorted_ids, block_expert, num_padded, w13_p, w13_s_p, inter_bf16),
+      capacity(dims, block_m) / block_m, stream));
+}
+
+int moe_a16w4_forward(const moe_a8w4_dims* dims, const void* hidden, const int32_t* topk_ids,
+                      const float* topk_weights, const uint8_t* w13_p, const uint8_t* w13_s_p,
+                      const uint8_t* w2_p, const uint8_t* w2_s_p, void* out, void* workspace,
+                      size_t workspace_bytes, hipStream_t stream) {
+  int st = check_dims(dims);
+  if (st) return st;
+  if (dims->tokens == 0) return MOE_OK;
+  const void* ptrs[9] = {hidden, topk_ids, topk_weights, w13_p, w13_s_p, w2_p, w2_s_p, out, workspace};
+  for (const void* p : ptrs)
+    if (!p) return MOE_ERR_NULL;
+  const void* al[7] = {hidden, topk_ids, topk_weights, w13_p, w13_s_p, w2_p, out};
+  for (const void* p : al)
+    if (!aligned(p, 16)) return MOE_ERR_ALIGN;
+  if (!aligned(w2_s_p, 16) || !aligned(workspace, 256)) return MOE_ERR_ALIGN;
+  const int bm = a16_bm(dims);
+  const A16Layout L = a16_layout(dims, bm);
+  if (workspace_bytes < L.total) return MOE_ERR_WORKSPACE;
+  uint8_t* ws = static_cast<uint8_t*>(workspace);
+  int32_t* sorted = reinterpret_cast<int32_t*>(ws + L.sorted);
+  int32_t* bexp = reinterpret_cast<int32_t*>(ws + L.bexp);
+  int32_t* npad = reinterpret_cast<int32_t*>(ws + L.npad);
+  uint8_t* inter = ws + L.inter;
+  uint8_t* y = ws + L.y;
+  const int64_t max_blocks = capacity(dims, bm) / bm;
+  // the sort alone (no activation quantiser), stage one, stage two, combine
+  hipError_t e = moe::launch_prep(topk_ids, dims->tokens, dims->topk, dims->num_experts,
+                                  dims->expert_offset, bm, sorted, bexp, npad, nullptr, 0, nullptr,
+                                  nullptr, moe::RouteArgs{}, stream);
+  if (e != hipSuccess) return status_of(e);
+  e = moe::launch_a16_stage1(
+      a16_stage1_args(dims, bm, hidden, sorted, bexp, npad, w13_p, w13_s_p, inter), max_blocks, stream);
+  if (e != hipSuccess) return status_of(e);
+  GemmArgs a2 = stage2_args(dims, bm, inter, nullptr, sorted, bexp, npad, topk_weights, w2_p, w2_s_p, y);
+  e = moe::launch_a16_stage2(a2, max_blocks, stream);
+  if (e != hipSuccess) return status_of(e);
+  return status_of(moe::launch_combine(dims->tokens, dims->hidden, dims->topk, dims->num_experts,
+                                       dims->expert_offset, topk_ids, reinterpret_cast<int16_t*>(y),
+                                       y + route_codes_bytes(dims), static_cast<uint16_t*>(out), stream));
 }
 
 const char* moe_a8w4_status_str(int status) {

@@ -15,7 +15,8 @@ the workloads the pages measure:
     top-6, token counts 1 ... 16384, random routing.
   * aiter PR 6286 "Retune gfx942 a16w4 DSv4.1 tiles for Triton 3.8", the
     isolated-kernel tables: 385 experts top-7 with a fused shared expert, and
-    round-robin top-k routing.
+    round-robin top-k routing; its A16W4 sizes (w1 N 1536 K 5120, w2 N 5120
+    K 768, 384 top-6 and 385 top-7, M = 12 ... 16384).
 
 Distributions (no trained weights exist here, so all are synthetic):
   weights  E2M1 codes uniform over the 16 codes, E8M0 scale codes uniform over
@@ -69,6 +70,11 @@ WORKLOADS = {
                             (1, 4, 16, 64, 256, 1024, 4096, 16384), ("softmax",), 4),
     "prefill-shared": Workload("prefill-shared", 5120, 640, 576, 385, 384, 7, True, 0,
                                (4096, 16384), ("roundrobin", "softmax"), 5),
+    # the A16W4 variant (BF16 activations): w1 N = 1536, K = 5120; w2 N = 5120, K = 768
+    "a16w4-backbone": Workload("a16w4-backbone", 5120, 768, 768, 384, 384, 6, False, 0,
+                               (12, 256, 1024, 1536, 4096, 16384), ("roundrobin",), 6),
+    "a16w4-shared": Workload("a16w4-shared", 5120, 768, 768, 385, 384, 7, True, 0,
+                             (12, 256, 1024, 1536, 4096, 16384), ("roundrobin",), 7),
 }
 
 # the decode buckets of the backbone geometry (the boundary counts are parity cases)

@@ -15,7 +15,7 @@ HEADER = os.path.join(ROOT, "include", "moe_a8w4.h")
 def declared_functions():
     text = open(HEADER).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(moe_a8w4_[a-z_0-9]+)\s*\(", text)))
+    return sorted(set(re.findall(r"\b(moe_a(?:8|16)w4_[a-z_0-9]+)\s*\(", text)))
 
 
 def test_library_exports_every_declared_symbol():
