@@ -30,8 +30,10 @@ def a16_forward(layer, hidden, ids, wts, out=None):
     return abi.moe_a16w4_forward(layer.dims(M), x, i, g, *layer.packed, out=out)
 
 
+# block_m 16 (8 experts, 9 tokens; 6 experts, 1 token), 32 (24 experts, 60
+# tokens; 385-expert form scaled, 12 tokens), 64 (8 experts, 48 tokens)
 SMALL = [("a16w4-backbone", 8, 8, 9), ("a16w4-backbone", 24, 24, 60), ("a16w4-shared", 9, 8, 12),
-         ("a16w4-backbone", 6, 6, 1)]
+         ("a16w4-backbone", 6, 6, 1), ("a16w4-backbone", 8, 8, 48)]
 
 
 @pytest.mark.parametrize("name,E,routed,M", SMALL)
@@ -96,7 +98,8 @@ def test_a16_forward_small_all_tokens(name, E, routed, M):
     assert np.all(got[nolocal] == 0)
 
 
-FULL = [("a16w4-backbone", 12), ("a16w4-backbone", 256), ("a16w4-backbone", 1024), ("a16w4-shared", 12)]
+FULL = [("a16w4-backbone", 12), ("a16w4-backbone", 256), ("a16w4-backbone", 1024), ("a16w4-backbone", 4096),
+        ("a16w4-shared", 12)]
 
 
 @pytest.fixture(scope="module")
