@@ -90,6 +90,8 @@ def test_block_m_capacity_and_workspace_sizes():
     assert abi.moe_a8w4_block_m(dims(tokens=656, num_experts=96, topk=6)) == 128   # 41
     d.routed_experts = 384
     assert abi.moe_a8w4_block_m(d) == 32
+    assert abi.moe_a8w4_block_m(dims(tokens=320, num_experts=96, topk=6)) == 32    # 20 per expert
+    assert abi.moe_a8w4_block_m(dims(tokens=336, num_experts=96, topk=6)) == 64    # 21
     d.routed_experts = -1
     assert abi.load().moe_a8w4_block_m(ctypes.byref(d)) == abi.MOE_ERR_DIMS
     d = dims(tokens=33, num_experts=384, topk=6)
