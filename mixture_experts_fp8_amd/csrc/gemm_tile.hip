@@ -140,13 +140,23 @@ constexpr int kComputeWaves = 8, kLoaderWaves = 4;
 constexpr int kScalePreloadBytes = 32 * 1024;
 
 // PRE: the tile's token scales are preloaded (BM x K/32 <= kScalePreloadBytes).
-template <int STAGE, int CGW, int S, bool PRE>
+// SC4 (without PRE): token scales come four steps at a time, one 16-byte load
+// per token every fourth step into a double-buffered area, instead of a
+// 4-byte gather per token and step (a quarter of those L2 requests); needs
+// K/128 a multiple of 4 (stage one: K = H, a multiple of 512) and 16-byte
+// aligned scale rows.
+template <int STAGE, int CGW, int S, bool PRE, bool SC4 = false>
 __global__ void __launch_bounds__(64 * (kComputeWaves + kLoaderWaves), 3) tile_kernel(GemmArgs args) {
   using G = TileGeom<CGW>;
   constexpr int BM = G::BM;
+  static_assert(!(PRE && SC4), "one way of loading token scales");
+  static_assert(!SC4 || S <= 5, "a scale buffer is refilled once its four steps are read");
   __shared__ __attribute__((aligned(1024))) uint8_t smem[S][G::BYTES];
   // all token scales of the tile, [BM tokens][K / 32], when they fit
   __shared__ __attribute__((aligned(16))) uint8_t spre[PRE ? kScalePreloadBytes : 16];
+  // SC4: [2 buffers][BM tokens][4 steps][4 scale bytes]; buffer q & 1 holds
+  // steps 4q .. 4q + 3
+  __shared__ __attribute__((aligned(16))) uint8_t ssc[SC4 ? 2 * BM * 16 : 16];
 
   const int N = args.N, K = args.K, M = args.M;
   const int KS = K / 128;
@@ -216,7 +226,13 @@ __global__ void __launch_bounds__(64 * (kComputeWaves + kLoaderWaves), 3) tile_k
 #pragma unroll
       for (int i = 0; i < G::NBCH; ++i) dma16(gB[i] + s * 128, base + G::B + (l * G::NBCH + i) * 1024);
       dma4(gAs + (int64_t)s * 256, base + G::AS + l * 256);
-      if (has_bs) dma4(gBs + 4 * s, base + G::BS + l * 256);
+      if (has_bs) {
+        if constexpr (SC4) {
+          if ((s & 3) == 0) dma16(gBs + 4 * s, lds_addr(&ssc[0]) + (uint32_t)((s >> 2) & 1) * (BM * 16) + l * 1024);
+        } else {
+          dma4(gBs + 4 * s, base + G::BS + l * 256);
+        }
+      }
     };
 #pragma unroll
     for (int s = 0; s < S - 1; ++s)
@@ -225,8 +241,21 @@ __global__ void __launch_bounds__(64 * (kComputeWaves + kLoaderWaves), 3) tile_k
       // barrier s publishes step s: it has landed once at most the loads of
       // steps s+1 .. s+S-2 are outstanding (near the end: none)
       if (s + S - 2 < KS) {
-        if (has_bs) __builtin_amdgcn_s_waitcnt(vmcnt_only((S - 2) * (G::LOADS + 1)));
-        else __builtin_amdgcn_s_waitcnt(vmcnt_only((S - 2) * G::LOADS));
+        if (has_bs) {
+          if constexpr (SC4) {
+            // steps s+1 .. s+S-2 (at most 3 of them) hold at most one
+            // scale load, the one of a step that is a multiple of 4
+            bool sc = false;
+#pragma unroll
+            for (int j = 1; j <= S - 2; ++j) sc = sc || ((s + j) & 3) == 0;
+            if (sc) __builtin_amdgcn_s_waitcnt(vmcnt_only((S - 2) * G::LOADS + 1));
+            else __builtin_amdgcn_s_waitcnt(vmcnt_only((S - 2) * G::LOADS));
+          } else {
+            __builtin_amdgcn_s_waitcnt(vmcnt_only((S - 2) * (G::LOADS + 1)));
+          }
+        } else {
+          __builtin_amdgcn_s_waitcnt(vmcnt_only((S - 2) * G::LOADS));
+        }
       } else {
         __builtin_amdgcn_s_waitcnt(vmcnt_only(0));
       }
@@ -294,7 +323,9 @@ __global__ void __launch_bounds__(64 * (kComputeWaves + kLoaderWaves), 3) tile_k
         const uint8_t* row = base + G::B + tok * 128;
         bb[i] = join8(*reinterpret_cast<const v4i*>(row + ((g ^ sw) << 4)),
                       *reinterpret_cast<const v4i*>(row + (((4 + g) ^ sw) << 4)));
-        sb[i] = PRE ? spre[(tok * KS + s) * 4 + g] : base[G::BS + tok * 4 + g];
+        sb[i] = PRE ? spre[(tok * KS + s) * 4 + g]
+                    : SC4 ? ssc[((s >> 2) & 1) * (BM * 16) + tok * 16 + (s & 3) * 4 + g]
+                          : base[G::BS + tok * 4 + g];
       };
       // step s with its weight fragments in cur and its first column group
       // in bb[P]; when NEXT (s + 1 < KS) also takes barrier s + 1 and reads
@@ -604,6 +635,8 @@ void launch_one(const GemmArgs& a, dim3 g, dim3 blk, hipStream_t stream) {
   }
   if (CGW == 2 && 32 * CGW * (a.K / 128) * 4 <= kScalePreloadBytes)
     hipLaunchKernelGGL((tile_kernel<STAGE, CGW, S, true>), g, blk, 0, stream, a);
+  else if (STAGE == 1 && (a.K / 128) % 4 == 0 && ((uintptr_t)a.bs & 15) == 0)
+    hipLaunchKernelGGL((tile_kernel<STAGE, CGW, S, false, true>), g, blk, 0, stream, a);
   else
     hipLaunchKernelGGL((tile_kernel<STAGE, CGW, S, false>), g, blk, 0, stream, a);
 }
