@@ -242,7 +242,7 @@ int64_t moe_a8w4_fused_counters(const moe_a8w4_dims* dims, int32_t block_m);
  * dequantised w13 (FP32 accumulation), the intermediate SiLU(gate) * up is
  * rounded to BF16 (nearest, ties to even), stage two multiplies it by w2,
  * and the routing-weighted routes are combined as in moe_a8w4_forward.
- * Blocks of 16, 32 or 64 routes (moe_a16w4_block_m); the weights are exact in
+ * Blocks of 16, 32, 64 or 128 routes (moe_a16w4_block_m); the weights are exact in
  * BF16 for every scale code whose products stay normal (codes 1 ... 254
  * with |element| >= 0.5 scaled above 2^-126).  Four launches: sort, stage
  * one, stage two, combine.  Errors, ownership and stream rules as
@@ -255,11 +255,11 @@ int moe_a16w4_forward(const moe_a8w4_dims* dims, const void* hidden, const int32
 /* Bytes of workspace moe_a16w4_forward needs for these dims. */
 int moe_a16w4_workspace_bytes(const moe_a8w4_dims* dims, size_t* bytes);
 
-/* Rows per sorted block (16, 32 or 64) that moe_a16w4_forward uses. */
+/* Rows per sorted block (16, 32, 64 or 128) that moe_a16w4_forward uses. */
 int moe_a16w4_block_m(const moe_a8w4_dims* dims);
 
 /* Stage one of the A16W4 variant for every sorted block (sort buffers from
- * moe_a8w4_sort with this block_m, 16, 32 or 64): inter_bf16 [capacity, I] BF16,
+ * moe_a8w4_sort with this block_m, 16, 32, 64 or 128): inter_bf16 [capacity, I] BF16,
  * row p = sorted position, holding BF16(SiLU(gate) * up); rows of blocks
  * that hold a route are written in full. */
 int moe_a16w4_stage1(const moe_a8w4_dims* dims, int32_t block_m, const void* hidden,

@@ -128,15 +128,15 @@ moe::FusedArgs fused_args(const moe_a8w4_dims* d, int bm, int32_t* cnt, const in
 }
 
 // A16W4 variant: blocks of 16 routes while an expert averages at most 8, 32
-// up to 32, else 64 (its kernel keeps a block's tokens in registers; blocks
-// of 64 halve the weight re-reads of large calls: 16384 tokens 7 % faster,
-// but cost more than they save while most experts fill half a block: with
-// the shared expert, 1536 tokens (24 routes per routed expert) took 1156 us
-// in blocks of 64 against 892 in blocks of 32).
+// up to 32 (the register-blocked kernel), 64 up to 64 and 128 beyond (the
+// LDS-tiled kernel).  Measured: with the shared expert, 1536 tokens (24
+// routes per routed expert) took 1156 us in blocks of 64 of the register
+// kernel against 892 in blocks of 32; 384 experts top-6, 16384 tokens: 2851
+// us in blocks of 64 of the tiled kernel, 2515 in blocks of 128.
 int a16_bm(const moe_a8w4_dims* d) {
   const int experts = d->routed_experts > d->num_experts ? d->routed_experts : d->num_experts;
   const double avg = (double)d->tokens * d->topk / experts;
-  return avg <= 8.0 ? 16 : avg <= 32.0 ? 32 : 64;
+  return avg <= 8.0 ? 16 : avg <= 32.0 ? 32 : avg <= 64.0 ? 64 : 128;
 }
 
 struct A16Layout {
@@ -459,7 +459,7 @@ int moe_a16w4_stage1(const moe_a8w4_dims* dims, int32_t block_m, const void* hid
                      const uint8_t* w13_p, const uint8_t* w13_s_p, void* inter_bf16, hipStream_t stream) {
   int st = check_dims(dims);
   if (st) return st;
-  if (block_m != 16 && block_m != 32 && block_m != 64) return MOE_ERR_BLOCK_M;
+  if (block_m != 16 && block_m != 32 && block_m != 64 && block_m != 128) return MOE_ERR_BLOCK_M;
   if (dims->tokens == 0) return MOE_OK;
   const void* ptrs[7] = {hidden, sorted_ids, block_expert, num_padded, w13_p, w13_s_p, inter_bf16};
   for (const void* p : ptrs)

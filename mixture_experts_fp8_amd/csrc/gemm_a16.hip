@@ -26,48 +26,12 @@ namespace moe {
 
 namespace {
 
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-
 template <int NCG>
 struct FragA16 {
   v4i a[4];          // weight codes of the 4 tiles, 32 FP4 each
   uint32_t sa;       // the 4 tiles' E8M0 scale bytes
   v4i b[NCG][4];     // token row K [32 (l/16) + 8j, +8) for j = 0..3, 8 BF16 each
 };
-
-// 2^(code - 127) as an fp32 (code 0: the subnormal 2^-127)
-__device__ __forceinline__ float e8m0_to_f32(uint32_t code) {
-  return __uint_as_float(code ? code << 23 : 0x00400000u);
-}
-
-// 8 FP4 codes (one 32-bit word, element 0 in the low nibble) to 8 BF16 times
-// the scale
-__device__ __forceinline__ bf16x8 fp4x8_to_bf16(uint32_t w, float scale) {
-  v4i r;
-  r.x = __builtin_bit_cast(int, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, scale, 0));
-  r.y = __builtin_bit_cast(int, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, scale, 1));
-  r.z = __builtin_bit_cast(int, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, scale, 2));
-  r.w = __builtin_bit_cast(int, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, scale, 3));
-  return __builtin_bit_cast(bf16x8, r);
-}
-
-// Stage-one epilogue of the A16W4 variant: as stage1_store, but the
-// intermediate is the BF16 (nearest, ties to even) of SiLU(gate) * up; lane
-// (t16, g) writes the 8 consecutive columns 32 grp + 8 g .. + 7 of row p.
-__device__ __forceinline__ void a16_stage1_store(const v4f acc[4], int64_t p, int grp, int I, int g,
-                                                 uint16_t* __restrict__ inter) {
-  uint32_t hb[8];
-#pragma unroll
-  for (int t = 0; t < 4; ++t)
-#pragma unroll
-    for (int q = 0; q < 2; ++q) {
-      const float gate = acc[t][2 * q], up = acc[t][2 * q + 1];
-      hb[2 * t + q] = f32_to_bf16(gate * __builtin_amdgcn_rcpf(1.0f + __expf(-gate)) * up);
-    }
-  const v4i v = {(int)(hb[0] | (hb[1] << 16)), (int)(hb[2] | (hb[3] << 16)), (int)(hb[4] | (hb[5] << 16)),
-                 (int)(hb[6] | (hb[7] << 16))};
-  *reinterpret_cast<v4i*>(inter + p * I + grp * 32 + 8 * g) = v;
-}
 
 // STAGE 1 or 2; NCG column groups of 16 tokens; NWK waves splitting K
 // (4 / NWK row groups per workgroup); a ring of PD fragments per wave.
@@ -227,16 +191,18 @@ hipError_t launch_a16_t(const GemmArgs& a, int64_t max_blocks, hipStream_t strea
 }  // namespace
 
 // Stage one at blocks of 16 splits K (H) over the four waves, as the A8W4
-// decode kernel does; at 32 and 64 each wave takes a row group over the whole
-// K, so the workgroup's four waves read the same token rows at the same steps
-// (served once from L1): 384 experts top-6, 1024 tokens 539 -> 532 us, 16384
-// tokens (blocks of 64) 5703 -> 5280 us.  Stage two keeps one wave per row
-// group (K = I, a few steps).
+// decode kernel does; at 32 each wave takes a row group over the whole K, so
+// the workgroup's four waves read the same token rows at the same steps
+// (served once from L1): 384 experts top-6, 1024 tokens 539 -> 532 us.
+// Stage two keeps one wave per row group (K = I, a few steps).
+// Blocks of 64 and 128 run the LDS-tiled kernel (gemm_tile.hip): 384 experts
+// top-6, 4096 tokens (blocks of 64) 1346 us here against 838 us there.
 hipError_t launch_a16_stage1(const GemmArgs& a, int64_t max_blocks, hipStream_t stream) {
   switch (a.bm) {
     case 16: return launch_a16_t<1, 1, 4>(a, max_blocks, stream);
     case 32: return launch_a16_t<1, 2, 1>(a, max_blocks, stream);
-    case 64: return launch_a16_t<1, 4, 1>(a, max_blocks, stream);
+    case 64:
+    case 128: return launch_a16_tile(1, a, max_blocks, stream);
     default: return hipErrorInvalidValue;
   }
 }
@@ -245,7 +211,8 @@ hipError_t launch_a16_stage2(const GemmArgs& a, int64_t max_blocks, hipStream_t 
   switch (a.bm) {
     case 16: return launch_a16_t<2, 1, 1>(a, max_blocks, stream);
     case 32: return launch_a16_t<2, 2, 1>(a, max_blocks, stream);
-    case 64: return launch_a16_t<2, 4, 1>(a, max_blocks, stream);
+    case 64:
+    case 128: return launch_a16_tile(2, a, max_blocks, stream);
     default: return hipErrorInvalidValue;
   }
 }

@@ -130,4 +130,46 @@ __device__ __forceinline__ void stage2_store(const v4f acc[4], int64_t slot, flo
   wave_lds_sync();
 }
 
+// ------------------------------------------------ A16W4 variant pieces
+//
+// BF16 activations x MXFP4 weights (gemm_a16.hip, and the tile kernel in
+// gemm_tile.hip): the FP4 weights are converted to BF16 in registers for the
+// BF16 MFMA, and stage one rounds its SiLU(gate) * up to a BF16 intermediate.
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+
+// 2^(code - 127) as an fp32 (code 0: the subnormal 2^-127)
+__device__ __forceinline__ float e8m0_to_f32(uint32_t code) {
+  return __uint_as_float(code ? code << 23 : 0x00400000u);
+}
+
+// 8 FP4 codes (one 32-bit word, element 0 in the low nibble) to 8 BF16 times
+// the scale
+__device__ __forceinline__ bf16x8 fp4x8_to_bf16(uint32_t w, float scale) {
+  v4i r;
+  r.x = __builtin_bit_cast(int, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, scale, 0));
+  r.y = __builtin_bit_cast(int, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, scale, 1));
+  r.z = __builtin_bit_cast(int, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, scale, 2));
+  r.w = __builtin_bit_cast(int, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, scale, 3));
+  return __builtin_bit_cast(bf16x8, r);
+}
+
+// Stage-one epilogue of the A16W4 variant: as stage1_store, but the
+// intermediate is the BF16 (nearest, ties to even) of SiLU(gate) * up; lane
+// (t16, g) writes the 8 consecutive columns 32 grp + 8 g .. + 7 of row p.
+__device__ __forceinline__ void a16_stage1_store(const v4f acc[4], int64_t p, int grp, int I, int g,
+                                                 uint16_t* __restrict__ inter) {
+  uint32_t hb[8];
+#pragma unroll
+  for (int t = 0; t < 4; ++t)
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+      const float gate = acc[t][2 * q], up = acc[t][2 * q + 1];
+      hb[2 * t + q] = f32_to_bf16(gate * __builtin_amdgcn_rcpf(1.0f + __expf(-gate)) * up);
+    }
+  const v4i v = {(int)(hb[0] | (hb[1] << 16)), (int)(hb[2] | (hb[3] << 16)), (int)(hb[4] | (hb[5] << 16)),
+                 (int)(hb[6] | (hb[7] << 16))};
+  *reinterpret_cast<v4i*>(inter + p * I + grp * 32 + 8 * g) = v;
+}
+
 }  // namespace moe

@@ -618,6 +618,181 @@ int resident_slices(const GemmArgs& a, int64_t max_tiles) {
   return pick;
 }
 
+// ------------------------------------------- A16W4 variant: BF16 tokens
+//
+// The tile kernel above for the A16W4 variant (BF16 activations x MXFP4
+// weights): the same workgroup tile (256 weight rows x BM tokens), waves
+// (8 compute, 4 loaders), ring of S K steps filled by direct loads and
+// expert-major tile order.  Per K step of 128: 16 KB of packed weights,
+// BM x 256 B of BF16 tokens and 1 KB of weight scales; no token scales.
+// A compute wave reads its 4 tiles' FP4 fragments from LDS, converts them to
+// BF16 (v_cvt_scalef32_pk_bf16_fp4 with the block scale) and runs
+// v_mfma_f32_16x16x32_bf16, four per tile and column group, with the K
+// assignment of gemm_a16.hip (MFMA j of a step takes K 32 q + 8 j + [0, 8) in
+// lane group q).  Token piece p (16 B, 8 BF16) of token t sits in slot
+// p ^ (t & 15): the 16 lanes of one operand read (16 tokens, one piece) hit
+// 16 distinct 16-byte bank slots.
+template <int CGW>
+struct TileGeomA16 {
+  static constexpr int BM = 32 * CGW;               // tokens
+  static constexpr int NBCH = 2 * CGW;              // 1 KB token chunks per loader and step
+  static constexpr int A = 0;
+  static constexpr int B = A + 16384;
+  static constexpr int AS = B + BM * 256;
+  static constexpr int BYTES = AS + 1024;
+  static constexpr int LOADS = 4 + NBCH + 1;        // per loader and step: A, B chunks, As
+};
+
+template <int STAGE, int CGW, int S>
+__global__ void __launch_bounds__(64 * (kComputeWaves + kLoaderWaves), 3) a16_tile_kernel(GemmArgs args) {
+  using G = TileGeomA16<CGW>;
+  constexpr int BM = G::BM;
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[S][G::BYTES];
+
+  const int N = args.N, K = args.K, M = args.M;
+  const int KS = K / 128;
+  const int NT = N / 256;
+  const int nblk = *args.num_padded / BM;
+  const int T = nblk * NT;
+  if ((int)blockIdx.x >= T) return;
+  int b, wgt;
+  expert_major(xcd_tile(blockIdx.x, T), NT, nblk, args.block_expert, b, wgt);
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int32_t* ids = args.sorted_ids + (int64_t)b * BM;
+
+  if (wave >= kComputeWaves) {
+    // ------------------------------------------------------------ loader
+    const int l = wave - kComputeWaves;
+    const int e = args.block_expert[b];
+    const int first = ids[0];
+    auto brow = [&](int t) -> int64_t {
+      if (STAGE == 1) {
+        const int r = ids[t];
+        return (int64_t)((r == M ? first : r) & 0xFFFFFF);
+      }
+      return (int64_t)b * BM + t;
+    };
+    const uint8_t* gA = args.w + (int64_t)e * ((int64_t)N * K / 2) +
+                        (int64_t)(wgt * 4 + l) * KS * 4096 + lane * 16;
+    const uint8_t* gAs = args.ws + (int64_t)e * ((int64_t)N * K / 32) +
+                         (int64_t)(wgt * 4 + l) * KS * 256 + lane * 4;
+    // chunk i of loader l: tokens 4 (l NBCH + i) + lane / 16, LDS slot
+    // lane % 16 of the token, filled with the piece that belongs there
+    const uint8_t* gB[G::NBCH];
+#pragma unroll
+    for (int i = 0; i < G::NBCH; ++i) {
+      const int t = 4 * (l * G::NBCH + i) + (lane >> 4);
+      const int piece = (lane & 15) ^ (t & 15);
+      gB[i] = args.bq + brow(t) * K * 2 + piece * 16;
+    }
+    const uint32_t lds0 = lds_addr(&smem[0][0]);
+    auto issue = [&](int s) {
+      const uint32_t base = lds0 + (uint32_t)(s % S) * G::BYTES;
+#pragma unroll
+      for (int t = 0; t < 4; ++t)
+        dma16(gA + (int64_t)s * 4096 + t * 1024, base + G::A + l * 4096 + t * 1024);
+#pragma unroll
+      for (int i = 0; i < G::NBCH; ++i) dma16(gB[i] + s * 256, base + G::B + (l * G::NBCH + i) * 1024);
+      dma4(gAs + (int64_t)s * 256, base + G::AS + l * 256);
+    };
+#pragma unroll
+    for (int s = 0; s < S - 1; ++s)
+      if (s < KS) issue(s);
+    for (int s = 0; s < KS; ++s) {
+      if (s + S - 2 < KS) __builtin_amdgcn_s_waitcnt(vmcnt_only((S - 2) * G::LOADS));
+      else __builtin_amdgcn_s_waitcnt(vmcnt_only(0));
+      barrier_only();
+      if (s + S - 1 < KS) issue(s + S - 1);
+    }
+    return;
+  }
+
+  // -------------------------------------------------------------- compute
+  const int wr = wave >> 1, wc = wave & 1;
+  const int t16 = lane & 15, g = lane >> 4;
+  int nact = 0;
+#pragma unroll
+  for (int c = 0; c < CGW; ++c)
+    if (__ballot(ids[wc * CGW * 16 + c * 16 + t16] != M) != 0) nact = c + 1;
+  nact = __builtin_amdgcn_readfirstlane(nact);
+
+  int64_t slot[CGW];
+  float wt[CGW];
+#pragma unroll
+  for (int c = 0; c < CGW; ++c) {
+    slot[c] = -1;
+    wt[c] = 0.f;
+    if (STAGE == 2) {
+      const int rid = ids[wc * CGW * 16 + c * 16 + t16];
+      if (rid != M) {
+        slot[c] = route_slot(rid, args.topk);
+        wt[c] = args.topk_weights[slot[c]];
+      }
+    }
+  }
+  v4f acc[4][CGW];
+#pragma unroll
+  for (int t = 0; t < 4; ++t)
+#pragma unroll
+    for (int c = 0; c < CGW; ++c) acc[t][c] = v4f{0.f, 0.f, 0.f, 0.f};
+
+  for (int s = 0; s < KS; ++s) {
+    barrier_only();   // barrier s publishes step s
+    if (nact > 0) {
+      const uint8_t* base = smem[s % S];
+      v4i a[4];
+#pragma unroll
+      for (int t = 0; t < 4; ++t) a[t] = *reinterpret_cast<const v4i*>(base + G::A + wr * 4096 + t * 1024 + lane * 16);
+      const uint32_t sa = *reinterpret_cast<const uint32_t*>(base + G::AS + wr * 256 + lane * 4);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        bf16x8 aj[4];
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+          const uint32_t w = (uint32_t)(j == 0 ? a[t].x : j == 1 ? a[t].y : j == 2 ? a[t].z : a[t].w);
+          aj[t] = fp4x8_to_bf16(w, e8m0_to_f32((sa >> (8 * t)) & 0xFFu));
+        }
+#pragma unroll
+        for (int c = 0; c < CGW; ++c) {
+          if (c < nact) {
+            const int tok = wc * CGW * 16 + c * 16 + t16;
+            const int slot_j = (4 * g + j) ^ (tok & 15);
+            const bf16x8 bj = __builtin_bit_cast(bf16x8, *reinterpret_cast<const v4i*>(base + G::B + tok * 256 + slot_j * 16));
+#pragma unroll
+            for (int t = 0; t < 4; ++t) acc[t][c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aj[t], bj, acc[t][c], 0, 0, 0);
+          }
+        }
+      }
+    }
+    // every LDS read of step s is done before barrier s + 1 frees its slot
+    __builtin_amdgcn_s_waitcnt(lgkmcnt_zero());
+  }
+
+  const int grp = wgt * 4 + wr;
+  if constexpr (STAGE == 1) {
+#pragma unroll
+    for (int c = 0; c < CGW; ++c) {
+      if (c < nact) {
+        const v4f part[4] = {acc[0][c], acc[1][c], acc[2][c], acc[3][c]};
+        a16_stage1_store(part, (int64_t)b * BM + wc * CGW * 16 + c * 16 + t16, grp, N / 2, g,
+                         reinterpret_cast<uint16_t*>(args.out_q));
+      }
+    }
+  } else {
+    // route rows through LDS scratch in a ring slot no wave reads after the
+    // last barrier (the slots of steps KS - 3 and KS - 2, or unused ones)
+    uint8_t* scr = smem[(KS + (wave >> 2)) % S] + (wave & 3) * kStage2Scratch;
+#pragma unroll
+    for (int c = 0; c < CGW; ++c) {
+      if (c < nact) {
+        const v4f part[4] = {acc[0][c], acc[1][c], acc[2][c], acc[3][c]};
+        stage2_store(part, slot[c], wt[c], args, grp, g, scr);
+      }
+    }
+  }
+}
+
 // Token-resident kernel where resident_slices allows, else tile_kernel. Its
 // scale preload pays at block_m 64 (stage one at local-slice M=4096: -6 %); at
 // block_m 128 the wait before step 0 costs more than the per-step gathers it
@@ -642,6 +817,19 @@ void launch_one(const GemmArgs& a, dim3 g, dim3 blk, hipStream_t stream) {
 }
 
 }  // namespace
+
+hipError_t launch_a16_tile(int stage, const GemmArgs& a, int64_t max_blocks, hipStream_t stream) {
+  constexpr int S = MOE_TILE_STAGES;
+  const int64_t grid = max_blocks * (a.N / 256);
+  if (grid <= 0) return hipSuccess;
+  const dim3 g((unsigned)grid), blk(64 * (kComputeWaves + kLoaderWaves));
+  if (stage == 1 && a.bm == 128) hipLaunchKernelGGL((a16_tile_kernel<1, 4, S>), g, blk, 0, stream, a);
+  else if (stage == 1 && a.bm == 64) hipLaunchKernelGGL((a16_tile_kernel<1, 2, S>), g, blk, 0, stream, a);
+  else if (stage == 2 && a.bm == 128) hipLaunchKernelGGL((a16_tile_kernel<2, 4, S>), g, blk, 0, stream, a);
+  else if (stage == 2 && a.bm == 64) hipLaunchKernelGGL((a16_tile_kernel<2, 2, S>), g, blk, 0, stream, a);
+  else return hipErrorInvalidValue;
+  return hipGetLastError();
+}
 
 hipError_t launch_tile(int stage, const GemmArgs& a, int64_t max_blocks, hipStream_t stream) {
   constexpr int S = MOE_TILE_STAGES;

@@ -80,6 +80,8 @@ hipError_t launch_fused(const GemmArgs& a1, const GemmArgs& a2, const FusedArgs&
 // intermediate [capacity, I] to a.out_q from BF16 rows a.bq; stage two reads it
 hipError_t launch_a16_stage1(const GemmArgs& a, int64_t max_blocks, hipStream_t stream);
 hipError_t launch_a16_stage2(const GemmArgs& a, int64_t max_blocks, hipStream_t stream);
+// its LDS-tiled form for bm = 64 or 128 (gemm_tile.hip)
+hipError_t launch_a16_tile(int stage, const GemmArgs& a, int64_t max_blocks, hipStream_t stream);
 // LDS-tiled variant of either stage for bm = 64 or 128 (gemm_tile.hip)
 hipError_t launch_tile(int stage, const GemmArgs& a, int64_t max_blocks, hipStream_t stream);
 

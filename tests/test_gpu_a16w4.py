@@ -31,9 +31,12 @@ def a16_forward(layer, hidden, ids, wts, out=None):
 
 
 # block_m 16 (8 experts, 9 tokens; 6 experts, 1 token), 32 (24 experts, 60
-# tokens; 385-expert form scaled, 12 tokens), 64 (8 experts, 48 tokens)
+# tokens; 385-expert form scaled, 12 tokens), 64 (8 experts, 48 tokens) and
+# 128 (8 experts, 100 tokens; 9 with the shared one, 90 tokens): the last two
+# run the LDS-tiled kernel
 SMALL = [("a16w4-backbone", 8, 8, 9), ("a16w4-backbone", 24, 24, 60), ("a16w4-shared", 9, 8, 12),
-         ("a16w4-backbone", 6, 6, 1), ("a16w4-backbone", 8, 8, 48)]
+         ("a16w4-backbone", 6, 6, 1), ("a16w4-backbone", 8, 8, 48), ("a16w4-backbone", 8, 8, 100),
+         ("a16w4-shared", 9, 8, 90)]
 
 
 @pytest.mark.parametrize("name,E,routed,M", SMALL)
@@ -99,7 +102,7 @@ def test_a16_forward_small_all_tokens(name, E, routed, M):
 
 
 FULL = [("a16w4-backbone", 12), ("a16w4-backbone", 256), ("a16w4-backbone", 1024), ("a16w4-backbone", 4096),
-        ("a16w4-shared", 12)]
+        ("a16w4-backbone", 16384), ("a16w4-shared", 12), ("a16w4-shared", 4096)]
 
 
 @pytest.fixture(scope="module")
