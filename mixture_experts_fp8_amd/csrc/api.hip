@@ -127,16 +127,17 @@ moe::FusedArgs fused_args(const moe_a8w4_dims* d, int bm, int32_t* cnt, const in
   return f;
 }
 
-// A16W4 variant: blocks of 16 routes while an expert averages at most 8, 32
-// up to 28 (the register-blocked kernel), 64 up to 64 and 128 beyond (the
-// LDS-tiled kernel).  Measured, 384 experts top-6: at 16 and 24 routes per
-// expert blocks of 32 beat the tiled kernel's 64 (530 against 562 us, 646
-// against 693), at 32 the tiled kernel wins (708 against 745); 16384
-// tokens: 2851 us in blocks of 64, 2515 in blocks of 128.
+// A16W4 variant: blocks of 16 routes while an expert averages at most 8 (the
+// register-blocked kernel), then the LDS-tiled kernel in blocks of 32 up to
+// 40, 64 up to 64 and 128 beyond.  Measured, 384 experts top-6: at 8 routes
+// per expert the register kernel's blocks of 16 beat the tiled kernel's 32
+// (447 against 487 us); at 32 blocks of 32 beat 64 (550 against 702); at 48
+// blocks of 64 beat 32 (759 against 818); 16384 tokens: 2851 us in blocks of
+// 64, 2515 in blocks of 128.
 int a16_bm(const moe_a8w4_dims* d) {
   const int experts = d->routed_experts > d->num_experts ? d->routed_experts : d->num_experts;
   const double avg = (double)d->tokens * d->topk / experts;
-  return avg <= 8.0 ? 16 : avg <= 28.0 ? 32 : avg <= 64.0 ? 64 : 128;
+  return avg <= 8.0 ? 16 : avg <= 40.0 ? 32 : avg <= 64.0 ? 64 : 128;
 }
 
 struct A16Layout {

@@ -190,17 +190,15 @@ hipError_t launch_a16_t(const GemmArgs& a, int64_t max_blocks, hipStream_t strea
 
 }  // namespace
 
-// Stage one at blocks of 16 splits K (H) over the four waves, as the A8W4
-// decode kernel does; at 32 each wave takes a row group over the whole K, so
-// the workgroup's four waves read the same token rows at the same steps
-// (served once from L1): 384 experts top-6, 1024 tokens 539 -> 532 us.
-// Stage two keeps one wave per row group (K = I, a few steps).
-// Blocks of 64 and 128 run the LDS-tiled kernel (gemm_tile.hip): 384 experts
-// top-6, 4096 tokens (blocks of 64) 1346 us here against 838 us there.
+// Blocks of 16 run here: stage one splits K (H) over the four waves, as the
+// A8W4 decode kernel does, stage two keeps one wave per row group (K = I, a
+// few steps).  Blocks of 32, 64 and 128 run the LDS-tiled kernel
+// (gemm_tile.hip): 384 experts top-6, 1536 tokens in blocks of 32 647 us here
+// against 541 us there, 4096 tokens in blocks of 64 1346 against 838.
 hipError_t launch_a16_stage1(const GemmArgs& a, int64_t max_blocks, hipStream_t stream) {
   switch (a.bm) {
     case 16: return launch_a16_t<1, 1, 4>(a, max_blocks, stream);
-    case 32: return launch_a16_t<1, 2, 1>(a, max_blocks, stream);
+    case 32:
     case 64:
     case 128: return launch_a16_tile(1, a, max_blocks, stream);
     default: return hipErrorInvalidValue;
@@ -210,7 +208,7 @@ hipError_t launch_a16_stage1(const GemmArgs& a, int64_t max_blocks, hipStream_t 
 hipError_t launch_a16_stage2(const GemmArgs& a, int64_t max_blocks, hipStream_t stream) {
   switch (a.bm) {
     case 16: return launch_a16_t<2, 1, 1>(a, max_blocks, stream);
-    case 32: return launch_a16_t<2, 2, 1>(a, max_blocks, stream);
+    case 32:
     case 64:
     case 128: return launch_a16_tile(2, a, max_blocks, stream);
     default: return hipErrorInvalidValue;

@@ -825,6 +825,8 @@ hipError_t launch_a16_tile(int stage, const GemmArgs& a, int64_t max_blocks, hip
   const dim3 g((unsigned)grid), blk(64 * (kComputeWaves + kLoaderWaves));
   if (stage == 1 && a.bm == 128) hipLaunchKernelGGL((a16_tile_kernel<1, 4, S>), g, blk, 0, stream, a);
   else if (stage == 1 && a.bm == 64) hipLaunchKernelGGL((a16_tile_kernel<1, 2, S>), g, blk, 0, stream, a);
+  else if (stage == 1 && a.bm == 32) hipLaunchKernelGGL((a16_tile_kernel<1, 1, S>), g, blk, 0, stream, a);
+  else if (stage == 2 && a.bm == 32) hipLaunchKernelGGL((a16_tile_kernel<2, 1, S>), g, blk, 0, stream, a);
   else if (stage == 2 && a.bm == 128) hipLaunchKernelGGL((a16_tile_kernel<2, 4, S>), g, blk, 0, stream, a);
   else if (stage == 2 && a.bm == 64) hipLaunchKernelGGL((a16_tile_kernel<2, 2, S>), g, blk, 0, stream, a);
   else return hipErrorInvalidValue;
