@@ -12,7 +12,9 @@
 // E8M0 scale: exact for every scale whose products stay normal in BF16) and
 // feeds v_mfma_f32_16x16x32_bf16.  Mapping as in gemm.hip ("swap-AB"):
 // weights are the A matrix, tokens the B matrix, a wave owns 64 weight rows
-// (4 tiles of 16) and the block's bm tokens; a wave step covers 128 K.
+// (4 tiles of 16) and the block's bm tokens; a wave step covers 128 K.  This
+// file runs blocks of 16 routes (decode sizes); larger blocks run the
+// LDS-tiled form of the variant in gemm_tile.hip.
 //
 // K inside a step: lane l of the packed weights holds the 32 elements
 // K [32 (l/16), +32) of its row.  MFMA j (j = 0..3) of the step takes
