@@ -137,3 +137,61 @@ def test_a16_forward_full_size_sampled(name, M, full_layers):
     tok = np.random.default_rng(M).choice(M, min(6, M), replace=False)
     ref = oracle.a16_forward(hidden, ids, wts, *L.host, tokens=tok)
     assert_gate(got[tok], wl.bf16_to_f32(ref), "a16w4 %s M=%d sampled" % (name, M))
+
+
+def test_a16_expert_offset():
+    """A local slice that does not start at expert 0: ids outside
+    [offset, offset + E) are skipped, tokens with none get zero rows."""
+    w = wl.scaled(wl.WORKLOADS["a16w4-backbone"], num_experts=16, routed_experts=64, expert_offset=24,
+                  config_id=431)
+    L = Layer(w)
+    M = 24
+    hidden, ids, wts = wl.make_inputs(w, M, "softmax")
+    note("a16 expert offset 24, E=16 of 64, M=%d bm=%d" % (M, abi.moe_a16w4_block_m(L.dims(M))))
+    out = a16_forward(L, dev(hidden), dev(ids), dev(wts))
+    torch.cuda.synchronize()
+    got = out.float().cpu().numpy()
+    ref = oracle.a16_forward(hidden, ids, wts, *L.host, expert_offset=24)
+    assert_gate(got, wl.bf16_to_f32(ref), "a16w4 expert offset")
+    nolocal = ~(((ids >= 24) & (ids < 40)).any(axis=1))
+    assert nolocal.any() and np.all(got[nolocal] == 0)
+
+
+def test_a16_graph_replay_on_changed_inputs():
+    """One captured moe_a16w4_forward replayed on original, changed and
+    restored inputs written into the captured buffers (blocks of 16 and, at
+    the second size, of the tiled kernel): every replay equals the eager call
+    bit for bit."""
+    for E, M in ((16, 12), (8, 60)):
+        w = wl.scaled(wl.WORKLOADS["a16w4-backbone"], num_experts=E, routed_experts=E, config_id=440 + M)
+        L = Layer(w)
+        d = L.dims(M)
+        note("a16 graph replay E=%d M=%d bm=%d" % (E, M, abi.moe_a16w4_block_m(d)))
+        cases = {"original": wl.make_inputs(w, M, "softmax", seed=[1]),
+                 "changed": wl.make_inputs(w, M, "softmax", seed=[2])}
+        cases["restored"] = cases["original"]
+        ws = torch.empty(abi.moe_a16w4_workspace_bytes(d), dtype=torch.uint8, device=DEV)
+        xd, idd, wd = (dev(a) for a in cases["original"])
+        out = torch.empty((M, w.hidden), dtype=torch.bfloat16, device=DEV)
+        s = torch.cuda.Stream()
+        s.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(s):
+            abi.moe_a16w4_forward(d, xd, idd, wd, *L.packed, out=out, workspace=ws)
+        torch.cuda.current_stream().wait_stream(s)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            abi.moe_a16w4_forward(d, xd, idd, wd, *L.packed, out=out, workspace=ws)
+        torch.cuda.synchronize()
+        for name, (h, i, wt) in cases.items():
+            xd.copy_(dev(h))
+            idd.copy_(dev(i))
+            wd.copy_(dev(wt))
+            torch.cuda.synchronize()
+            g.replay()
+            torch.cuda.synchronize()
+            got = out.clone()
+            eager = abi.moe_a16w4_forward(d, dev(h), dev(i), dev(wt), *L.packed)
+            torch.cuda.synchronize()
+            assert torch.equal(got.view(torch.int16), eager.view(torch.int16)), name
+        del g
