@@ -506,7 +506,8 @@ def main():
         a = b["alg"]
         s1 = float(np.mean(s1_us[:, bi]))
         per_bucket[str(b["M"])] = dict(
-            us_per_call=round(us, 2), routes=a["R"], experts_touched=a["D"], block_m=b["bm"],
+            us_per_call=round(us, 2), us_p10=round(float(np.percentile(ts, 10)), 2),
+            us_p90=round(float(np.percentile(ts, 90)), 2), routes=a["R"], experts_touched=a["D"], block_m=b["bm"],
             GBps=round(a["bytes"] / us / 1e3, 1), hbm_frac=round(a["bytes"] / us / 1e3 / HBM_PEAK_GBS, 4),
             TFLOPs=round(a["flops"] / us / 1e6, 2), stage1_us=round(s1, 2),
             stage1_GBps=round(a["stage1_bytes"] / s1 / 1e3, 1))
