@@ -143,3 +143,50 @@ def test_router_entry_points_validate():
     d.topk = 1                                                                        # shared slot only
     assert lib.moe_a8w4_forward_routed(ctypes.byref(d), p, p, 15, *([p] * 8), 1 << 30, None) \
         == abi.MOE_ERR_DIMS
+
+
+def test_a16w4_entry_points_validate():
+    """The A16W4 variant: bad dims, null or misaligned pointers, a small
+    workspace, bad block_m; M = 0 succeeds without touching anything."""
+    lib = abi.load()
+    p, odd = ctypes.c_void_p(4096), ctypes.c_void_p(4096 + 8)
+    d = dims(tokens=12, num_experts=384, topk=6, inter=768)
+    need = abi.moe_a16w4_workspace_bytes(d)
+    assert need > 0 and abi.moe_a16w4_block_m(d) == 16
+    assert abi.moe_a16w4_block_m(dims(tokens=1536, num_experts=384, topk=6, inter=768)) == 32   # 24
+    assert abi.moe_a16w4_block_m(dims(tokens=4096, num_experts=384, topk=6, inter=768)) == 64   # 64
+    assert abi.moe_a16w4_block_m(dims(tokens=16384, num_experts=384, topk=6, inter=768)) == 128
+    bad = dims(inter=576)
+    n = ctypes.c_size_t(0)
+    assert lib.moe_a16w4_workspace_bytes(ctypes.byref(bad), ctypes.byref(n)) == abi.MOE_ERR_DIMS
+    assert lib.moe_a16w4_forward(ctypes.byref(bad), *([p] * 9), need, None) == abi.MOE_ERR_DIMS
+    for i in range(9):
+        ptrs = [p] * 9
+        ptrs[i] = None
+        assert lib.moe_a16w4_forward(ctypes.byref(d), *ptrs, need, None) == abi.MOE_ERR_NULL
+    assert lib.moe_a16w4_forward(ctypes.byref(d), odd, *([p] * 8), need, None) == abi.MOE_ERR_ALIGN
+    assert lib.moe_a16w4_forward(ctypes.byref(d), *([p] * 8), ctypes.c_void_p(4096 + 16), need, None) \
+        == abi.MOE_ERR_ALIGN
+    assert lib.moe_a16w4_forward(ctypes.byref(d), *([p] * 9), need - 1, None) == abi.MOE_ERR_WORKSPACE
+    z = dims(tokens=0, inter=768)
+    assert lib.moe_a16w4_forward(ctypes.byref(z), *([None] * 9), 0, None) == abi.MOE_OK
+    assert lib.moe_a16w4_stage1(ctypes.byref(d), 48, *([p] * 7), None) == abi.MOE_ERR_BLOCK_M
+    assert lib.moe_a16w4_stage1(ctypes.byref(d), 16, *([p] * 6), None, None) == abi.MOE_ERR_NULL
+
+
+def test_fused_launch_entry_points_validate():
+    """moe_a8w4_stages_fused: block_m 16 or 32 only, every pointer required,
+    the counter count grows with the tokens."""
+    lib = abi.load()
+    p = ctypes.c_void_p(4096)
+    d = dims(tokens=6, num_experts=384, topk=6)
+    n6 = abi.moe_a8w4_fused_counters(d, 16)
+    assert n6 > 0 and abi.moe_a8w4_fused_counters(dims(tokens=12, num_experts=384, topk=6), 16) > n6
+    assert lib.moe_a8w4_fused_counters(ctypes.byref(d), 64) == abi.MOE_ERR_BLOCK_M
+    assert lib.moe_a8w4_stages_fused(ctypes.byref(d), 64, *([p] * 16), None) == abi.MOE_ERR_BLOCK_M
+    for i in range(16):
+        ptrs = [p] * 16
+        ptrs[i] = None
+        assert lib.moe_a8w4_stages_fused(ctypes.byref(d), 16, *ptrs, None) == abi.MOE_ERR_NULL
+    z = dims(tokens=0)
+    assert lib.moe_a8w4_stages_fused(ctypes.byref(z), 16, *([None] * 16), None) == abi.MOE_OK
