@@ -39,8 +39,9 @@ __device__ __forceinline__ float exp2_neg(int E) {
 
 // Route rows (stage two's per-route outputs, summed by the top-k combine).
 // Each 32 consecutive outputs of a route share an exponent byte S: the fp32
-// exponent field of their largest magnitude, at least 14.  Output v is stored
-// as the 16-bit integer RNE(v * 2^(140 - S)), which lies in [-2^14, 2^14],
+// exponent field of their largest magnitude (as fp32), at least 14.  Output
+// v (the routing weight times the fp32 accumulator, an exact product) is
+// stored as the 16-bit integer RNE(v * 2^(140 - S)), which lies in [-2^14, 2^14],
 // and decodes exactly to code * 2^(S - 140); the rounding error is at most
 // 2^-14 of the block's largest magnitude (blocks below 2^-112 keep 2^-127
 // absolute).  Finite values only.
@@ -52,6 +53,14 @@ __device__ __forceinline__ int route_block_exp(float amax) {
 // 2^(140 - S) and 2^(S - 140) as fp32 (S in [14, 254]).
 __device__ __forceinline__ float route_encode_mul(int S) { return __uint_as_float((uint32_t)(267 - S) << 23); }
 __device__ __forceinline__ float route_decode_mul(int S) { return __uint_as_float((uint32_t)(S - 13) << 23); }
+
+// The code of x * m (|x m| <= 2^14) in the low 16 bits of the result: one
+// fused multiply-add onto 1.5 * 2^23 rounds the exact product to the nearest
+// integer, ties to even (the sum's unit in the last place is 1), and leaves
+// it as a two's-complement offset in the low mantissa bits.
+__device__ __forceinline__ uint32_t route_code_bits(float x, float m) {
+  return __float_as_uint(__builtin_fmaf(x, m, 12582912.0f));
+}
 
 __device__ __forceinline__ float bf16_to_f32(uint32_t bits16) {
   return __uint_as_float(bits16 << 16);

@@ -95,23 +95,23 @@ template <bool COH = false>
 __device__ __forceinline__ void stage2_store(const v4f acc[4], int64_t slot, float wt, const GemmArgs& args,
                                              int grp, int g, uint8_t* scr) {
   const int lane = threadIdx.x & 63, t16 = lane & 15;
-  float v[16];
+  // the block maximum of |wt acc|: rounding is monotonic, so |wt| times the
+  // largest |acc| rounds to the largest rounded product
   float amax = 0.f;
 #pragma unroll
   for (int t = 0; t < 4; ++t)
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      v[4 * t + r] = wt * acc[t][r];
-      amax = fmaxf(amax, fabsf(v[4 * t + r]));
-    }
+    for (int r = 0; r < 4; ++r) amax = fmaxf(amax, fabsf(acc[t][r]));
+  amax = fabsf(wt) * amax;
   amax = fmaxf(amax, __shfl_xor(amax, 16));
   const int S = route_block_exp(amax);
-  const float mul = route_encode_mul(S);
+  const float wm = wt * route_encode_mul(S);   // exact: a power-of-two scaling
   uint32_t w[8];
 #pragma unroll
   for (int j = 0; j < 8; ++j) {
-    const int c0 = (int)__builtin_rintf(v[2 * j] * mul), c1 = (int)__builtin_rintf(v[2 * j + 1] * mul);
-    w[j] = ((uint32_t)c0 & 0xFFFFu) | ((uint32_t)c1 << 16);
+    const int i0 = 2 * j, i1 = 2 * j + 1;
+    w[j] = __builtin_amdgcn_perm(route_code_bits(acc[i1 >> 2][i1 & 3], wm), route_code_bits(acc[i0 >> 2][i0 & 3], wm),
+                                 0x05040100u);
   }
   uint8_t* row = scr + t16 * 144 + g * 32;
   *reinterpret_cast<v4i*>(row) = v4i{(int)w[0], (int)w[1], (int)w[2], (int)w[3]};
