@@ -91,9 +91,20 @@ constexpr int kStage2Scratch = 16 * 144;
 // wave's LDS scratch so that each store instruction writes 8 routes x 128 B
 // in a row instead of 32-byte pieces of 16 routes.  All 64 lanes must call it
 // together.  COH: another workgroup of the launch reads the rows.
+// The slots written by store q (q = 0, 1) of stage2_store in this lane: lane
+// l writes route 8 q + l / 8 of the column group, whose slot lane (route, g)
+// holds (negative: none).  Route slots stay below 2^27 (tokens below 2^24,
+// top-k at most 8), so 32 bits carry them.  A wave that stores several
+// slices of the same routes computes them once.
+__device__ __forceinline__ void stage2_store_slots(int64_t slot, int sl2[2]) {
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int q = 0; q < 2; ++q) sl2[q] = __shfl((int)slot, 8 * q + (lane >> 3));
+}
+
 template <bool COH = false>
-__device__ __forceinline__ void stage2_store(const v4f acc[4], int64_t slot, float wt, const GemmArgs& args,
-                                             int grp, int g, uint8_t* scr) {
+__device__ __forceinline__ void stage2_store(const v4f acc[4], int64_t slot, const int sl2[2], float wt,
+                                             const GemmArgs& args, int grp, int g, uint8_t* scr) {
   const int lane = threadIdx.x & 63, t16 = lane & 15;
   // the block maximum of |wt acc|: rounding is monotonic, so |wt| times the
   // largest |acc| rounds to the largest rounded product
@@ -118,16 +129,22 @@ __device__ __forceinline__ void stage2_store(const v4f acc[4], int64_t slot, flo
   *reinterpret_cast<v4i*>(row + 16) = v4i{(int)w[4], (int)w[5], (int)w[6], (int)w[7]};
   const int S1 = __shfl(S, t16 + 32);   // exponent of the second block (lane g = 2)
   wave_lds_sync();
-  const int slo = (int)(uint32_t)slot, shi = (int)(slot >> 32);
 #pragma unroll
   for (int q = 0; q < 2; ++q) {
     const int route = 8 * q + (lane >> 3), chunk = lane & 7;
-    const int64_t sl = ((int64_t)__shfl(shi, route) << 32) | (uint32_t)__shfl(slo, route);
     const v4i c = *reinterpret_cast<const v4i*>(scr + route * 144 + chunk * 16);
-    if (sl >= 0) st128<COH>(args.y_codes + sl * args.N + grp * 64 + chunk * 8, c);
+    if (sl2[q] >= 0) st128<COH>(args.y_codes + (int64_t)sl2[q] * args.N + grp * 64 + chunk * 8, c);
   }
   if (g == 0 && slot >= 0) st16<COH>(args.y_exps + slot * (args.N / 32) + 2 * grp, (uint16_t)(S | (S1 << 8)));
   wave_lds_sync();
+}
+
+template <bool COH = false>
+__device__ __forceinline__ void stage2_store(const v4f acc[4], int64_t slot, float wt, const GemmArgs& args,
+                                             int grp, int g, uint8_t* scr) {
+  int sl2[2];
+  stage2_store_slots(slot, sl2);
+  stage2_store<COH>(acc, slot, sl2, wt, args, grp, g, scr);
 }
 
 // ------------------------------------------------ A16W4 variant pieces

@@ -536,6 +536,12 @@ __global__ void __launch_bounds__(64 * (kComputeWaves + kLoaderWaves), 3) tile_r
         wt[c] = rid == M ? 0.f : args.topk_weights[slot[c]];
       }
     }
+    // the store lanes' route slots, the same for every slice
+    int sl2[NA > 0 ? NA : 1][2];
+    if constexpr (STAGE == 2) {
+#pragma unroll
+      for (int c = 0; c < NA; ++c) stage2_store_slots(slot[c], sl2[c]);
+    }
     for (int j = 0; j < NS; ++j) {
       v4f acc[4][NA > 0 ? NA : 1];
 #pragma unroll
@@ -577,7 +583,7 @@ __global__ void __launch_bounds__(64 * (kComputeWaves + kLoaderWaves), 3) tile_r
           const int col = wc * CGW * 16 + c * 16 + t16;
           stage1_store(part, (int64_t)b * BM + col, grp, N / 2, g, args.out_q, args.out_s);
         } else {
-          stage2_store(part, slot[c], wt[c], args, grp, g, scr);
+          stage2_store(part, slot[c], sl2[c], wt[c], args, grp, g, scr);
         }
       }
     }
