@@ -544,11 +544,10 @@ __global__ void __launch_bounds__(64 * (kComputeWaves + kLoaderWaves), 3) tile_r
     }
     for (int j = 0; j < NS; ++j) {
       v4f acc[4][NA > 0 ? NA : 1];
-#pragma unroll
-      for (int t = 0; t < 4; ++t)
-#pragma unroll
-        for (int c = 0; c < NA; ++c) acc[t][c] = v4f{0.f, 0.f, 0.f, 0.f};
-      for (int ks = 0; ks < KS; ++ks) {
+      // K step ks of slice j; the first step of a slice starts its
+      // accumulators from a literal zero (no per-slice register clearing)
+      auto kstep = [&](int ks, auto first_tag) {
+        constexpr bool FIRST = decltype(first_tag)::value;
         const int q = j * KS + ks;
         __builtin_amdgcn_s_waitcnt(lgkmcnt_zero());
         barrier_only();
@@ -560,6 +559,7 @@ __global__ void __launch_bounds__(64 * (kComputeWaves + kLoaderWaves), 3) tile_r
             a[t] = *reinterpret_cast<const v4i*>(base + wr * 4096 + t * 1024 + lane * 16);
           const uint32_t sa = *reinterpret_cast<const uint32_t*>(base + 16384 + wr * 256 + lane * 4);
           const uint8_t* bstep = sB + ks * BM * 128;
+          const v4f zero = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
           for (int c = 0; c < NA; ++c) {
             const int tok = wc * CGW * 16 + c * 16 + t16;
@@ -568,13 +568,15 @@ __global__ void __launch_bounds__(64 * (kComputeWaves + kLoaderWaves), 3) tile_r
             const v8i bb = join8(*reinterpret_cast<const v4i*>(row + ((g ^ sw) << 4)),
                                  *reinterpret_cast<const v4i*>(row + (((4 + g) ^ sw) << 4)));
             const uint32_t sb = sBs[(tok * KS + ks) * 4 + g];
-            acc[0][c] = mfma_fp4_fp8<0>(a[0], bb, acc[0][c], sa, sb);
-            acc[1][c] = mfma_fp4_fp8<1>(a[1], bb, acc[1][c], sa, sb);
-            acc[2][c] = mfma_fp4_fp8<2>(a[2], bb, acc[2][c], sa, sb);
-            acc[3][c] = mfma_fp4_fp8<3>(a[3], bb, acc[3][c], sa, sb);
+            acc[0][c] = mfma_fp4_fp8<0>(a[0], bb, FIRST ? zero : acc[0][c], sa, sb);
+            acc[1][c] = mfma_fp4_fp8<1>(a[1], bb, FIRST ? zero : acc[1][c], sa, sb);
+            acc[2][c] = mfma_fp4_fp8<2>(a[2], bb, FIRST ? zero : acc[2][c], sa, sb);
+            acc[3][c] = mfma_fp4_fp8<3>(a[3], bb, FIRST ? zero : acc[3][c], sa, sb);
           }
         }
-      }
+      };
+      kstep(0, std::true_type{});
+      for (int ks = 1; ks < KS; ++ks) kstep(ks, std::false_type{});
       const int grp = (sg * NS + j) * 4 + wr;
 #pragma unroll
       for (int c = 0; c < NA; ++c) {
