@@ -8,11 +8,14 @@ with gcc, loads it, and marshals numpy arrays to it.
 
 Sources of what is computed (page titles and sections):
   * aiter PR 5609 "Add DeepSeek V4.1 Flash TP4 gfx950 MoE tuning",
-    Configuration -- BF16 output, FP8 activations, MXFP4 weights, per-1x32
-    scaling, interleaved gate/up, SiLU, routing weight kept out of stage one.
+    Configuration: the number formats (8-bit float activations, 4-bit MX
+    weights, one shared scale per run of 32), the gate and up rows stored
+    alternately, a SiLU gate, and a result in bfloat16 with the routing
+    probabilities entering only after the down projection.
   * aiter PR 5904 "Add tuned a8w4 fused-MoE configs for DeepSeek V4.1-Flash
-    (TP4 + EP, gfx950)", "Fused-MoE kernel, expert-parallel benchmark" -- one
-    call is sorting, both stages and the intermediate quantization.
+    (TP4 + EP, gfx950)", "Fused-MoE kernel, expert-parallel benchmark": what
+    one timed call spans -- grouping routes by expert, the two GEMMs, and the
+    re-quantisation between them.
   * OCP Microscaling Formats v1.0 (E2M1, E8M0) and OCP 8-bit Floating Point
     v1.0 (E4M3) for the number formats those pages name.
 """
@@ -32,11 +35,13 @@ _lib = None
 
 
 def build(force: bool = True) -> str:
-    """Compile the oracle with gcc (-O2, OpenMP) next to its source."""
+    """Compile the oracle with gcc (-O3, OpenMP) next to its source.  ISO C99
+    mode keeps floating-point contraction off, so the result does not depend
+    on the optimisation level."""
     if force or not os.path.exists(_LIB):
         tmp = _LIB + ".tmp%d" % os.getpid()
         subprocess.check_call(
-            ["gcc", "-O2", "-std=c99", "-fopenmp", "-fPIC", "-shared",
+            ["gcc", "-O3", "-std=c99", "-fopenmp", "-fPIC", "-shared",
              "-Wall", "-Wextra", "-o", tmp, _SRC, "-lm"])
         os.replace(tmp, _LIB)
     return _LIB
@@ -76,16 +81,22 @@ def _load():
                                    + [vp, c_i64, vp, vp])
     lib.oracle_forward.restype = None
     lib.oracle_intermediate.argtypes = ([c_i64, c_i64, c_i64, c_int, c_int, c_int] + [vp] * 4
-                                        + [vp, c_i64, vp, vp, vp])
+                                        + [vp, c_i64, vp, vp, vp, vp, vp])
     lib.oracle_intermediate.restype = None
     lib.oracle_forward_given_intermediate.argtypes = ([c_i64, c_i64, c_i64, c_int, c_int, c_int]
-                                                      + [vp] * 4 + [vp, c_i64, vp, vp, vp, vp])
+                                                      + [vp] * 4 + [vp, c_i64, vp, vp, vp, vp, vp])
     lib.oracle_forward_given_intermediate.restype = None
-    lib.oracle_a16_stage1.argtypes = [c_i64, c_i64, vp, vp, vp, vp, vp]
+    lib.oracle_a16_stage1.argtypes = [c_i64, c_i64, vp, vp, vp, vp, vp, vp]
     lib.oracle_a16_stage1.restype = None
     lib.oracle_a16_forward.argtypes = ([c_i64, c_i64, c_i64, c_int, c_int, c_int] + [vp] * 7
                                        + [vp, c_i64, vp, vp, vp])
     lib.oracle_a16_forward.restype = None
+    lib.oracle_a16_intermediate.argtypes = ([c_i64, c_i64, c_i64, c_int, c_int, c_int] + [vp] * 4
+                                            + [vp, c_i64, vp, vp, vp])
+    lib.oracle_a16_intermediate.restype = None
+    lib.oracle_a16_forward_given_intermediate.argtypes = ([c_i64, c_i64, c_i64, c_int, c_int, c_int]
+                                                          + [vp] * 4 + [vp, c_i64, vp, vp, vp])
+    lib.oracle_a16_forward_given_intermediate.restype = None
     lib.oracle_softmax_topk.argtypes = [c_i64, c_int, c_int, c_int, vp, vp, vp]
     lib.oracle_softmax_topk.restype = None
     lib.oracle_num_threads.argtypes = []
@@ -227,8 +238,52 @@ def a16_stage1(x_bf16_row, w13_e, w13_s_e):
     I = w13_e.shape[0] // 2
     h = np.zeros(I, np.float64)
     hb = np.zeros(I, np.uint16)
-    _load().oracle_a16_stage1(H, I, _p(x), _p(w13_e), _p(w13_s_e), _p(h), _p(hb))
+    _load().oracle_a16_stage1(H, I, _p(x), _p(w13_e), _p(w13_s_e), None, _p(h), _p(hb))
     return h, hb
+
+
+def a16_intermediate(hidden_bf16, topk_ids, w13, w13_s, routes, expert_offset: int = 0):
+    """A16W4 stage one for flat route indices -> (BF16 bits [n, I], SiLU(g) * u
+    FP64 [n, I], gate/up FP64 [n, 2I] with gate j at 2j and up j at 2j + 1)."""
+    x = _c(hidden_bf16, np.uint16)
+    ids = _c(topk_ids, np.int32)
+    w13 = _c(w13, np.uint8)
+    w13_s = _c(w13_s, np.uint8)
+    r = _c(routes, np.int64)
+    M, H = x.shape
+    k = ids.shape[1]
+    E = w13.shape[0]
+    I = w13.shape[1] // 2
+    n = r.shape[0]
+    hb = np.zeros((n, I), np.uint16)
+    h = np.zeros((n, I), np.float64)
+    gu = np.zeros((n, 2 * I), np.float64)
+    _load().oracle_a16_intermediate(M, H, I, E, expert_offset, k, _p(x), _p(ids), _p(w13), _p(w13_s),
+                                    _p(r), n, _p(gu), _p(h), _p(hb))
+    return hb, h, gu
+
+
+def a16_forward_given_intermediate(topk_ids, topk_weights, w2, w2_s, inter_bf16, expert_offset: int = 0,
+                                   tokens=None, want_f64: bool = False):
+    """A16W4 stage two and the combine applied to a given BF16 intermediate
+    [ntok, topk, I] (bits; non-local slots ignored) -> out_bf16 [ntok, H]
+    (and the FP64 combine if want_f64)."""
+    ids = _c(topk_ids, np.int32)
+    wts = _c(topk_weights, np.float32)
+    w2 = _c(w2, np.uint8)
+    w2_s = _c(w2_s, np.uint8)
+    inter = _c(inter_bf16, np.uint16)
+    M, k = ids.shape
+    E, H = w2.shape[0], w2.shape[1]
+    I = w2.shape[2] * 2
+    tok = None if tokens is None else _c(tokens, np.int64)
+    ntok = M if tokens is None else tok.shape[0]
+    assert inter.shape == (ntok, k, I)
+    out = np.zeros((ntok, H), np.uint16)
+    o64 = np.zeros((ntok, H), np.float64) if want_f64 else None
+    _load().oracle_a16_forward_given_intermediate(M, H, I, E, expert_offset, k, _p(ids), _p(wts), _p(w2),
+                                                  _p(w2_s), _p(tok), ntok, _p(inter), _p(o64), _p(out))
+    return (out, o64) if want_f64 else out
 
 
 def a16_forward(hidden_bf16, topk_ids, topk_weights, w13, w13_s, w2, w2_s,
@@ -262,8 +317,11 @@ def a16_forward(hidden_bf16, topk_ids, topk_weights, w13, w13_s, w2, w2_s,
 
 
 def intermediate(hidden_bf16, topk_ids, w13, w13_s, routes, expert_offset: int = 0,
-                 want_f64: bool = False):
-    """Requantised intermediate for flat route indices -> (iq u8 [n, I], is u8 [n, I/32])."""
+                 want_f64: bool = False, want_gu: bool = False):
+    """Requantised intermediate for flat route indices -> (iq u8 [n, I], is u8 [n, I/32]),
+    then h = SiLU(gate) * up FP64 [n, I] if want_f64, then the FP64 gate/up sums
+    [n, 2I] (gate j at 2j, up j at 2j + 1) and the sums of |a_k w_k| of the
+    same dot products [n, 2I] if want_gu."""
     x = _c(hidden_bf16, np.uint16)
     ids = _c(topk_ids, np.int32)
     w13 = _c(w13, np.uint8)
@@ -277,18 +335,27 @@ def intermediate(hidden_bf16, topk_ids, w13, w13_s, routes, expert_offset: int =
     iq = np.zeros((n, I), np.uint8)
     is_ = np.zeros((n, I // 32), np.uint8)
     h = np.zeros((n, I), np.float64) if want_f64 else None
+    gu = np.zeros((n, 2 * I), np.float64) if want_gu else None
+    gu_abs = np.zeros((n, 2 * I), np.float64) if want_gu else None
     _load().oracle_intermediate(M, H, I, E, expert_offset, k, _p(x), _p(ids), _p(w13), _p(w13_s),
-                                _p(r), n, _p(h), _p(iq), _p(is_))
-    return (iq, is_, h) if want_f64 else (iq, is_)
+                                _p(r), n, _p(gu), _p(gu_abs), _p(h), _p(iq), _p(is_))
+    res = (iq, is_)
+    if want_f64:
+        res += (h,)
+    if want_gu:
+        res += (gu, gu_abs)
+    return res
 
 
 def forward_given_intermediate(topk_ids, topk_weights, w2, w2_s, inter_q, inter_s,
-                               expert_offset: int = 0, tokens=None, want_f64: bool = False):
+                               expert_offset: int = 0, tokens=None, want_f64: bool = False,
+                               want_abs: bool = False):
     """Stage two and the combine applied to a given intermediate.
 
     inter_q [ntok, topk, I] / inter_s [ntok, topk, I/32] hold the requantised
     intermediate of each listed token's slots (non-local slots are ignored).
-    Returns out_bf16 [ntok, H] (and the FP64 combine if want_f64).
+    Returns out_bf16 [ntok, H], then the FP64 combine if want_f64, then if
+    want_abs the sum over local slots of |weight| * sum_j |inter_j w2[h, j]|.
     """
     ids = _c(topk_ids, np.int32)
     wts = _c(topk_weights, np.float32)
@@ -307,10 +374,16 @@ def forward_given_intermediate(topk_ids, topk_weights, w2, w2_s, inter_q, inter_
     assert iq.shape == (ntok, k, I) and is_.shape == (ntok, k, I // 32)
     out = np.zeros((ntok, H), np.uint16)
     o64 = np.zeros((ntok, H), np.float64) if want_f64 else None
+    oab = np.zeros((ntok, H), np.float64) if want_abs else None
     _load().oracle_forward_given_intermediate(M, H, I, E, expert_offset, k, _p(ids), _p(wts),
                                               _p(w2), _p(w2_s), _p(tok), ntok, _p(iq), _p(is_),
-                                              _p(o64), _p(out))
-    return (out, o64) if want_f64 else out
+                                              _p(o64), _p(out), _p(oab))
+    res = (out,)
+    if want_f64:
+        res += (o64,)
+    if want_abs:
+        res += (oab,)
+    return res if len(res) > 1 else out
 
 
 def softmax_topk(logits, k_routed: int, shared_id: int = -1):

@@ -7,13 +7,16 @@
  * baseline leg of the benchmark may load it.  It shares no code, header,
  * table or constant with the HIP library; the product path never calls it.
  *
- * What the layer is (aiter PR 5609, "Add DeepSeek V4.1 Flash TP4 gfx950 MoE
- * tuning", section Configuration): BF16 output, FP8 activations, MXFP4
- * weights, per-1x32 scaling, interleaved gate/up, SiLU, and no routing-weight
- * multiplication in stage one.  What one call contains (aiter PR 5904, "Add
- * tuned a8w4 fused-MoE configs for DeepSeek V4.1-Flash (TP4 + EP, gfx950)",
- * section "Fused-MoE kernel, expert-parallel benchmark"): sorting, both
- * stages and the intermediate quantization.
+ * The layer follows aiter PR 5609, "Add DeepSeek V4.1 Flash TP4 gfx950 MoE
+ * tuning", section Configuration: activations are 8-bit floats and expert
+ * weights 4-bit MX values, each run of 32 along the reduction sharing one
+ * power-of-two scale; the gate and up projections sit in alternate rows of
+ * one matrix; the gate goes through SiLU; the routing probability scales
+ * each route only after the down projection; the result is bfloat16.  The
+ * span of one call follows aiter PR 5904, "Add tuned a8w4 fused-MoE configs
+ * for DeepSeek V4.1-Flash (TP4 + EP, gfx950)", section "Fused-MoE kernel,
+ * expert-parallel benchmark": it groups routes by expert, runs both GEMMs
+ * and re-quantises the values passed between them.
  *
  * Number formats are the ones those names denote:
  *   E2M1 (MXFP4 element), E8M0 (MX block scale): OCP Microscaling Formats
@@ -249,13 +252,17 @@ static inline double mxfp4_elem(const uint8_t* codes, const uint8_t* scales,
  * local expert e.
  *   a_q/a_s : the token's quantised activation row (H codes, H/32 scales)
  *   w13/_s  : expert e's gate/up matrix [2I, H/2] and scales [2I, H/32]
+ *   gu      : out, 2I values: gate_j at 2j, up_j at 2j+1, in FP64 (may be NULL)
+ *   gu_abs  : out, 2I values: the sums of |a_k w_k| of the same dot products,
+ *             the scale an accumulation error of each is measured against
+ *             (may be NULL)
  *   h       : out, I values of SiLU(gate) * up in FP64 (may be NULL)
  *   iq, is  : out, the requantised intermediate (I codes, I/32 scales)
  */
 void oracle_stage1(int64_t H, int64_t I,
                    const uint8_t* a_q, const uint8_t* a_s,
                    const uint8_t* w13, const uint8_t* w13_s,
-                   double* h, uint8_t* iq, uint8_t* is)
+                   double* gu, double* gu_abs, double* h, uint8_t* iq, uint8_t* is)
 {
     e4m3_table_init();
     double* a = (double*)malloc(sizeof(double) * H);
@@ -265,10 +272,22 @@ void oracle_stage1(int64_t H, int64_t I,
 
     /* g_j from row 2j, u_j from row 2j+1; SiLU(g) * u */
     for (int64_t j = 0; j < I; ++j) {
-        double g = 0.0, u = 0.0;
+        double g = 0.0, u = 0.0, ga = 0.0, ua = 0.0;
         for (int64_t kk = 0; kk < H; ++kk) {
-            g += a[kk] * mxfp4_elem(w13, w13_s, H, 2 * j, kk);
-            u += a[kk] * mxfp4_elem(w13, w13_s, H, 2 * j + 1, kk);
+            double pg = a[kk] * mxfp4_elem(w13, w13_s, H, 2 * j, kk);
+            double pu = a[kk] * mxfp4_elem(w13, w13_s, H, 2 * j + 1, kk);
+            g += pg;
+            u += pu;
+            ga += fabs(pg);
+            ua += fabs(pu);
+        }
+        if (gu) {
+            gu[2 * j] = g;
+            gu[2 * j + 1] = u;
+        }
+        if (gu_abs) {
+            gu_abs[2 * j] = ga;
+            gu_abs[2 * j + 1] = ua;
         }
         hv[j] = g / (1.0 + exp(-g)) * u;
     }
@@ -281,18 +300,24 @@ void oracle_stage1(int64_t H, int64_t I,
 }
 
 /* Stage two for one route: y_h = sum_j inter_j * w2[e][h, j] in FP64, with
- * inter the dequantised intermediate (I codes, I/32 scales). */
+ * inter the dequantised intermediate (I codes, I/32 scales); y_abs (may be
+ * NULL) receives sum_j |inter_j * w2[e][h, j]|. */
 void oracle_stage2(int64_t H, int64_t I, const uint8_t* iq, const uint8_t* is,
-                   const uint8_t* w2, const uint8_t* w2_s, double* y)
+                   const uint8_t* w2, const uint8_t* w2_s, double* y, double* y_abs)
 {
     e4m3_table_init();
     double* iv = (double*)malloc(sizeof(double) * I);
     for (int64_t j = 0; j < I; ++j)
         iv[j] = g_e4m3_all[iq[j]] * g_e8m0_all[is[j / 32]];
     for (int64_t hh = 0; hh < H; ++hh) {
-        double acc = 0.0;
-        for (int64_t j = 0; j < I; ++j) acc += iv[j] * mxfp4_elem(w2, w2_s, I, hh, j);
+        double acc = 0.0, aa = 0.0;
+        for (int64_t j = 0; j < I; ++j) {
+            double p = iv[j] * mxfp4_elem(w2, w2_s, I, hh, j);
+            acc += p;
+            aa += fabs(p);
+        }
         y[hh] = acc;
+        if (y_abs) y_abs[hh] = aa;
     }
     free(iv);
 }
@@ -304,8 +329,8 @@ void oracle_route(int64_t H, int64_t I,
                   const uint8_t* w2, const uint8_t* w2_s,
                   double* h, uint8_t* iq, uint8_t* is, double* y)
 {
-    oracle_stage1(H, I, a_q, a_s, w13, w13_s, h, iq, is);
-    if (y) oracle_stage2(H, I, iq, is, w2, w2_s, y);
+    oracle_stage1(H, I, a_q, a_s, w13, w13_s, NULL, NULL, h, iq, is);
+    if (y) oracle_stage2(H, I, iq, is, w2, w2_s, y, NULL);
 }
 
 /* Combine: o[t] = sum over local slots k, ascending, of w[t,k] * y[t,k] in
@@ -388,12 +413,13 @@ void oracle_forward_given_intermediate(int64_t M, int64_t H, int64_t I, int E, i
                                        const uint8_t* w2, const uint8_t* w2_s,
                                        const int64_t* tokens, int64_t ntok,
                                        const uint8_t* inter_q, const uint8_t* inter_s,
-                                       double* out_f64, uint16_t* out_bf16)
+                                       double* out_f64, uint16_t* out_bf16, double* out_abs)
 {
     e4m3_table_init();
     if (!tokens) ntok = M;
     int64_t nroute = ntok * topk;
     double* y = (double*)calloc((size_t)(nroute > 0 ? nroute : 1) * H, sizeof(double));
+    double* ya = out_abs ? (double*)calloc((size_t)(nroute > 0 ? nroute : 1) * H, sizeof(double)) : NULL;
 #pragma omp parallel for schedule(dynamic, 1)
     for (int64_t r = 0; r < nroute; ++r) {
         int64_t i = r / topk, k = r % topk;
@@ -401,9 +427,27 @@ void oracle_forward_given_intermediate(int64_t M, int64_t H, int64_t I, int E, i
         int64_t le = (int64_t)topk_ids[t * topk + k] - expert_offset;
         if (le < 0 || le >= E) continue;
         oracle_stage2(H, I, inter_q + r * I, inter_s + r * (I / 32),
-                      w2 + le * H * (I / 2), w2_s + le * H * (I / 32), y + r * H);
+                      w2 + le * H * (I / 2), w2_s + le * H * (I / 32), y + r * H, ya ? ya + r * H : NULL);
     }
     combine(H, E, expert_offset, topk, topk_ids, topk_weights, tokens, ntok, y, out_f64, out_bf16);
+    if (out_abs) {
+        /* sum over local slots of |w[t,k]| * sum_j |inter_j w2[h, j]|: the
+         * scale the accumulation errors of stage two are measured against */
+#pragma omp parallel for schedule(static)
+        for (int64_t i = 0; i < ntok; ++i) {
+            int64_t t = tokens ? tokens[i] : i;
+            for (int64_t hh = 0; hh < H; ++hh) {
+                double o = 0.0;
+                for (int k = 0; k < topk; ++k) {
+                    int64_t le = (int64_t)topk_ids[t * topk + k] - expert_offset;
+                    if (le < 0 || le >= E) continue;
+                    o += fabs((double)topk_weights[t * topk + k]) * ya[(i * topk + k) * H + hh];
+                }
+                out_abs[i * H + hh] = o;
+            }
+        }
+        free(ya);
+    }
     free(y);
 }
 
@@ -422,10 +466,11 @@ void oracle_forward_given_intermediate(int64_t M, int64_t H, int64_t I, int E, i
  * Stage one for one route: h_j = BF16(SiLU(g_j) * u_j) with g_j, u_j the FP64
  * dot products of the token's BF16 row with rows 2j and 2j+1 of w13[e].
  *   x    the token's BF16 row (H values)
+ *   gu   out, 2I values: g_j at 2j, u_j at 2j+1 (may be NULL)
  *   h64  out, I values of SiLU(g) * u before the rounding (may be NULL)
  *   hb   out, I BF16 values of the intermediate */
 void oracle_a16_stage1(int64_t H, int64_t I, const uint16_t* x,
-                       const uint8_t* w13, const uint8_t* w13_s, double* h64, uint16_t* hb)
+                       const uint8_t* w13, const uint8_t* w13_s, double* gu, double* h64, uint16_t* hb)
 {
     e4m3_table_init();
     double* a = (double*)malloc(sizeof(double) * H);
@@ -437,6 +482,10 @@ void oracle_a16_stage1(int64_t H, int64_t I, const uint16_t* x,
             u += a[kk] * mxfp4_elem(w13, w13_s, H, 2 * j + 1, kk);
         }
         double h = g / (1.0 + exp(-g)) * u;
+        if (gu) {
+            gu[2 * j] = g;
+            gu[2 * j + 1] = u;
+        }
         if (h64) h64[j] = h;
         hb[j] = oracle_bf16_rne(h);
     }
@@ -481,7 +530,7 @@ void oracle_a16_forward(int64_t M, int64_t H, int64_t I, int E, int expert_offse
         if (le < 0 || le >= E) continue;
         uint16_t* hb = (uint16_t*)malloc(sizeof(uint16_t) * I);
         oracle_a16_stage1(H, I, hidden + t * H, w13 + le * (2 * I) * (H / 2),
-                          w13_s + le * (2 * I) * (H / 32), NULL, hb);
+                          w13_s + le * (2 * I) * (H / 32), NULL, NULL, hb);
         if (inter_bf16) memcpy(inter_bf16 + r * I, hb, sizeof(uint16_t) * I);
         oracle_a16_stage2(H, I, hb, w2 + le * H * (I / 2), w2_s + le * H * (I / 32), y + r * H);
         free(hb);
@@ -490,14 +539,68 @@ void oracle_a16_forward(int64_t M, int64_t H, int64_t I, int E, int expert_offse
     free(y);
 }
 
+/* The A16W4 intermediate of a list of routes (flat index f = t*topk+k): the
+ * BF16 values hb [nr, I], and optionally SiLU(g) * u before the rounding
+ * h_f64 [nr, I] and the gate/up sums gu_f64 [nr, 2I] (g_j at 2j, u_j at
+ * 2j + 1).  Non-local routes give all-zero rows. */
+void oracle_a16_intermediate(int64_t M, int64_t H, int64_t I, int E, int expert_offset, int topk,
+                             const uint16_t* hidden, const int32_t* topk_ids,
+                             const uint8_t* w13, const uint8_t* w13_s,
+                             const int64_t* routes, int64_t nr,
+                             double* gu_f64, double* h_f64, uint16_t* hb)
+{
+    e4m3_table_init();
+    (void)M;
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t r = 0; r < nr; ++r) {
+        int64_t f = routes[r], t = f / topk;
+        int64_t le = (int64_t)topk_ids[f] - expert_offset;
+        memset(hb + r * I, 0, sizeof(uint16_t) * I);
+        if (h_f64) memset(h_f64 + r * I, 0, sizeof(double) * I);
+        if (gu_f64) memset(gu_f64 + r * 2 * I, 0, sizeof(double) * 2 * I);
+        if (le < 0 || le >= E) continue;
+        oracle_a16_stage1(H, I, hidden + t * H, w13 + le * (2 * I) * (H / 2),
+                          w13_s + le * (2 * I) * (H / 32), gu_f64 ? gu_f64 + r * 2 * I : NULL,
+                          h_f64 ? h_f64 + r * I : NULL, hb + r * I);
+    }
+}
+
+/* Stage two and the combine of oracle_a16_forward applied to a given BF16
+ * intermediate inter [ntok, topk, I] of the listed tokens' slots (rows of
+ * non-local slots are ignored): to check the output given another
+ * implementation's intermediate. */
+void oracle_a16_forward_given_intermediate(int64_t M, int64_t H, int64_t I, int E, int expert_offset,
+                                           int topk, const int32_t* topk_ids, const float* topk_weights,
+                                           const uint8_t* w2, const uint8_t* w2_s,
+                                           const int64_t* tokens, int64_t ntok, const uint16_t* inter,
+                                           double* out_f64, uint16_t* out_bf16)
+{
+    e4m3_table_init();
+    if (!tokens) ntok = M;
+    int64_t nroute = ntok * topk;
+    double* y = (double*)calloc((size_t)(nroute > 0 ? nroute : 1) * H, sizeof(double));
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t r = 0; r < nroute; ++r) {
+        int64_t i = r / topk, k = r % topk;
+        int64_t t = tokens ? tokens[i] : i;
+        int64_t le = (int64_t)topk_ids[t * topk + k] - expert_offset;
+        if (le < 0 || le >= E) continue;
+        oracle_a16_stage2(H, I, inter + r * I, w2 + le * H * (I / 2), w2_s + le * H * (I / 32), y + r * H);
+    }
+    combine(H, E, expert_offset, topk, topk_ids, topk_weights, tokens, ntok, y, out_f64, out_bf16);
+    free(y);
+}
+
 /* The requantised intermediate of a list of routes (flat index f = t*topk+k),
  * for comparison with the stage-one output.  Routes that are not local give
- * all-zero rows.  h_f64 [nr, I] may be NULL. */
+ * all-zero rows.  h_f64 [nr, I] (SiLU(gate) * up), gu_f64 [nr, 2I] (gate
+ * and up, interleaved as the rows of w13) and gu_abs_f64 [nr, 2I] (the sums
+ * of |a_k w_k| of those dot products) may be NULL. */
 void oracle_intermediate(int64_t M, int64_t H, int64_t I, int E, int expert_offset, int topk,
                          const uint16_t* hidden, const int32_t* topk_ids,
                          const uint8_t* w13, const uint8_t* w13_s,
                          const int64_t* routes, int64_t nr,
-                         double* h_f64, uint8_t* iq, uint8_t* is)
+                         double* gu_f64, double* gu_abs_f64, double* h_f64, uint8_t* iq, uint8_t* is)
 {
     e4m3_table_init();
     (void)M;
@@ -508,6 +611,8 @@ void oracle_intermediate(int64_t M, int64_t H, int64_t I, int E, int expert_offs
         memset(iq + r * I, 0, I);
         memset(is + r * (I / 32), 0, I / 32);
         if (h_f64) memset(h_f64 + r * I, 0, sizeof(double) * I);
+        if (gu_f64) memset(gu_f64 + r * 2 * I, 0, sizeof(double) * 2 * I);
+        if (gu_abs_f64) memset(gu_abs_f64 + r * 2 * I, 0, sizeof(double) * 2 * I);
         if (le < 0 || le >= E) continue;
         uint8_t* aq = (uint8_t*)malloc(H);
         uint8_t* as = (uint8_t*)malloc(H / 32);
@@ -516,10 +621,10 @@ void oracle_intermediate(int64_t M, int64_t H, int64_t I, int E, int expert_offs
             for (int q = 0; q < 32; ++q) blk[q] = oracle_bf16_value(hidden[t * H + b * 32 + q]);
             oracle_quant_block(blk, 32, aq + b * 32, as + b);
         }
-        oracle_route(H, I, aq, as,
-                     w13 + le * (2 * I) * (H / 2), w13_s + le * (2 * I) * (H / 32),
-                     NULL, NULL,
-                     h_f64 ? h_f64 + r * I : NULL, iq + r * I, is + r * (I / 32), NULL);
+        oracle_stage1(H, I, aq, as,
+                      w13 + le * (2 * I) * (H / 2), w13_s + le * (2 * I) * (H / 32),
+                      gu_f64 ? gu_f64 + r * 2 * I : NULL, gu_abs_f64 ? gu_abs_f64 + r * 2 * I : NULL,
+                      h_f64 ? h_f64 + r * I : NULL, iq + r * I, is + r * (I / 32));
         free(aq); free(as);
     }
 }

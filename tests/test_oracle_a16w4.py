@@ -66,3 +66,54 @@ def test_a16_invariants(oracle):
     sub = np.array([5, 0, 3], np.int64)
     full = oracle.a16_forward(hidden, ids, wts, w13, w13_s, w2, w2_s)
     assert np.array_equal(oracle.a16_forward(hidden, ids, wts, w13, w13_s, w2, w2_s, tokens=sub), full[sub])
+
+
+def test_a16_intermediate_gate_up_equal_dense(oracle):
+    """oracle.a16_intermediate: the FP64 gate/up sums equal a numpy dense
+    product (single expert), SiLU(g) * u follows, and the BF16 values equal
+    the ones oracle.a16_forward passes to stage two."""
+    w = small(H=512, I=128, E=1, topk=1, cid=194)
+    w13, w13_s, w2, w2_s = wl.make_weights(w)
+    M = 4
+    hidden = wl.make_hidden(np.random.default_rng(9), M, 512)
+    ids = np.zeros((M, 1), np.int32)
+    wts = np.ones((M, 1), np.float32)
+    hb, h, gu = oracle.a16_intermediate(hidden, ids, w13, w13_s, np.arange(M))
+    X = ind.bf16_to_f64(hidden)
+    W13 = ind.dequant_mxfp4(w13[0], w13_s[0])
+    g, u = X @ W13[0::2].T, X @ W13[1::2].T
+    np.testing.assert_allclose(gu[:, 0::2], g, rtol=1e-12, atol=1e-12 * np.abs(g).max())
+    np.testing.assert_allclose(gu[:, 1::2], u, rtol=1e-12, atol=1e-12 * np.abs(u).max())
+    hd = g / (1.0 + np.exp(-g)) * u
+    np.testing.assert_allclose(h, hd, rtol=1e-12, atol=1e-12 * np.abs(hd).max())
+    _, inter = oracle.a16_forward(hidden, ids, wts, w13, w13_s, w2, w2_s, want_inter=True)
+    assert np.array_equal(hb, inter[:, 0])
+
+
+def test_a16_given_intermediate_reproduces_forward(oracle):
+    """Stage two + combine on the oracle's own BF16 intermediate is its
+    forward, bit for bit; one changed intermediate element moves the output by
+    exactly weight * w2[:, j] * delta."""
+    w = small(H=256, I=64, E=8, topk=3, cid=195)
+    w13, w13_s, w2, w2_s = wl.make_weights(w)
+    hidden, ids, wts = wl.make_inputs(w, 6, "softmax", seed=[195])
+    ids = ids.copy()
+    ids[1, 2] = -3                                        # a non-local slot
+    M, k = ids.shape
+    out, o64, inter = oracle.a16_forward(hidden, ids, wts, w13, w13_s, w2, w2_s, want_f64=True,
+                                         want_inter=True)
+    hb, _, _ = oracle.a16_intermediate(hidden, ids, w13, w13_s, np.arange(M * k))
+    assert np.array_equal(hb.reshape(M, k, -1), inter)
+    out2, o2 = oracle.a16_forward_given_intermediate(ids, wts, w2, w2_s, inter, want_f64=True)
+    assert np.array_equal(out2, out) and np.array_equal(o2, o64)
+    sub = np.array([4, 1], np.int64)
+    assert np.array_equal(oracle.a16_forward_given_intermediate(ids, wts, w2, w2_s, inter[sub], tokens=sub),
+                          out[sub])
+    inter2 = inter.copy()
+    inter2[0, 0, 7] ^= 0x0001                              # one BF16 step
+    _, o3 = oracle.a16_forward_given_intermediate(ids, wts, w2, w2_s, inter2, want_f64=True)
+    W2 = ind.dequant_mxfp4(w2[ids[0, 0]], w2_s[ids[0, 0]])
+    delta = ind.bf16_to_f64(inter2[0, 0, 7:8])[0] - ind.bf16_to_f64(inter[0, 0, 7:8])[0]
+    np.testing.assert_allclose(o3[0] - o64[0], float(wts[0, 0]) * W2[:, 7] * delta, rtol=1e-9,
+                               atol=1e-12 * np.abs(o64).max())
+    assert np.array_equal(o3[1:], o64[1:])

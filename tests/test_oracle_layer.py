@@ -15,7 +15,7 @@ def small(H=256, I=64, Iv=None, E=8, routed=None, topk=3, shared=False, offset=0
                        topk, shared, offset, (), ("softmax",), cid)
 
 
-def silu_mlp_dense(hidden_bits, w13e, w13se, w2e, w2se):
+def silu_mlp_dense(hidden_bits, w13e, w13se, w2e, w2se, want_gu=False):
     """Dense SiLU-gated MLP on dequantised operands (numpy FP64 matmuls), with
     the per-1x32 quantisation of the activations and of the intermediate done
     by the brute-force quantiser."""
@@ -30,6 +30,8 @@ def silu_mlp_dense(hidden_bits, w13e, w13se, w2e, w2se):
     iq, is_ = ind.quantize_rows_bruteforce(h)
     Hq = ind.dequant_fp8(iq, is_)
     W2 = ind.dequant_mxfp4(w2e, w2se)
+    if want_gu:
+        return Hq @ W2.T, iq, is_, g, u
     return Hq @ W2.T, iq, is_
 
 
@@ -42,10 +44,28 @@ def test_single_expert_top1_equals_dense_mlp(oracle, H, I, Iv, M):
     ids = np.zeros((M, 1), np.int32)
     wts = np.ones((M, 1), np.float32)
     out, o64 = oracle.forward(hidden, ids, wts, w13, w13_s, w2, w2_s, want_f64=True)
-    y, iq_ref, is_ref = silu_mlp_dense(hidden, w13[0], w13_s[0], w2[0], w2_s[0])
-    iq, is_ = oracle.intermediate(hidden, ids, w13, w13_s, np.arange(M))
+    y, iq_ref, is_ref, g, u = silu_mlp_dense(hidden, w13[0], w13_s[0], w2[0], w2_s[0], want_gu=True)
+    iq, is_, h, gu, gu_abs = oracle.intermediate(hidden, ids, w13, w13_s, np.arange(M), want_f64=True,
+                                                 want_gu=True)
     assert np.array_equal(iq, iq_ref)
     assert np.array_equal(is_, is_ref)
+    # the FP64 gate and up sums (gate j at 2j, up j at 2j + 1) and SiLU(gate) * up
+    np.testing.assert_allclose(gu[:, 0::2], g, rtol=1e-12, atol=1e-12 * np.abs(g).max())
+    np.testing.assert_allclose(gu[:, 1::2], u, rtol=1e-12, atol=1e-12 * np.abs(u).max())
+    hd = g / (1.0 + np.exp(-g)) * u
+    np.testing.assert_allclose(h, hd, rtol=1e-12, atol=1e-12 * np.abs(hd).max())
+    # the sums of |a_k w_k| of the same dot products
+    x = ind.bf16_to_f64(hidden)
+    A = np.abs(ind.dequant_fp8(*ind.quantize_rows_bruteforce(x)))
+    W13 = np.abs(ind.dequant_mxfp4(w13[0], w13_s[0]))
+    np.testing.assert_allclose(gu_abs[:, 0::2], A @ W13[0::2].T, rtol=1e-12)
+    np.testing.assert_allclose(gu_abs[:, 1::2], A @ W13[1::2].T, rtol=1e-12)
+    # stage two's absolute sum, weighted by |w| over the slots
+    _, o2, oab = oracle.forward_given_intermediate(ids, wts * -2, w2, w2_s, iq[:, None], is_[:, None],
+                                                   want_f64=True, want_abs=True)
+    Hq = np.abs(ind.dequant_fp8(iq, is_))
+    np.testing.assert_allclose(oab, 2 * Hq @ np.abs(ind.dequant_mxfp4(w2[0], w2_s[0])).T, rtol=1e-12)
+    np.testing.assert_allclose(o2, -2 * o64, rtol=1e-12, atol=1e-12 * np.abs(o64).max())
     np.testing.assert_allclose(o64, y, rtol=1e-12, atol=1e-12 * np.abs(y).max())
     # padded intermediate columns quantise to exact zeros
     assert np.all(iq[:, Iv:] == 0)
