@@ -3,14 +3,15 @@
  * (gfx950): FP8 E4M3 activations with per-1x32 E8M0 scales times MXFP4
  * (E2M1 + E8M0 per 1x32) expert weights, BF16 output.
  *
- * What one call computes is the layer of aiter PR 5609 ("Add DeepSeek V4.1
- * Flash TP4 gfx950 MoE tuning", section Configuration): BF16 output, FP8
- * activations, MXFP4 weights, per-1x32 scaling, interleaved gate/up, SiLU,
- * routing weight applied in stage two only; and it contains what the timed
- * call of aiter PR 5904 ("Add tuned a8w4 fused-MoE configs for
- * DeepSeek V4.1-Flash (TP4 + EP, gfx950)", section "Fused-MoE kernel,
- * expert-parallel benchmark") contains: sorting, both stages and the
- * intermediate quantization.
+ * One call computes the layer defined in aiter PR 5609 ("Add DeepSeek V4.1
+ * Flash TP4 gfx950 MoE tuning", section Configuration) -- 8-bit float
+ * activations against 4-bit MX expert weights with a power-of-two scale per
+ * 32 elements, gate and up rows alternating in one matrix, a SiLU gate, the
+ * routing probability applied after the down projection, a bfloat16
+ * result -- and spans what the timed call of aiter PR 5904 ("Add tuned a8w4
+ * fused-MoE configs for DeepSeek V4.1-Flash (TP4 + EP, gfx950)", section
+ * "Fused-MoE kernel, expert-parallel benchmark") spans: grouping the routes
+ * by expert, both GEMMs and the re-quantisation between them.
  *
  *   a_q, a_s  = per-1x32 quantisation of hidden (E8M0 exponent
  *               floor(log2 amax) - 8, clamped at -127; E4M3 elements rounded
@@ -205,8 +206,8 @@ int moe_a8w4_combine(const moe_a8w4_dims* dims, const int32_t* topk_ids, const v
 
 /* Stage one, stage two and the top-k combine of one call in a single launch
  * (block_m 16 or 32), the decode form of the layer after moe_a8w4_quant_sort
- * (aiter PR 5904, "Fused-MoE kernel, expert-parallel benchmark": one call
- * holds sorting, both stages and the intermediate quantization).  Results as
+ * (aiter PR 5904, "Fused-MoE kernel, expert-parallel benchmark": the timed
+ * call spans the grouping, both GEMMs and the re-quantisation).  Results as
  * moe_a8w4_stage1 (inter_q, inter_s), moe_a8w4_stage2 (y_routes) and
  * moe_a8w4_combine (out, every element written) with the same buffers.
  * A stage-two tile of a block starts streaming its weights at once and waits
@@ -265,6 +266,24 @@ int moe_a16w4_block_m(const moe_a8w4_dims* dims);
 int moe_a16w4_stage1(const moe_a8w4_dims* dims, int32_t block_m, const void* hidden,
                      const int32_t* sorted_ids, const int32_t* block_expert, const int32_t* num_padded,
                      const uint8_t* w13_p, const uint8_t* w13_s_p, void* inter_bf16, hipStream_t stream);
+
+/* ------------------------------------------------------ hardware probe */
+
+/* The scaled matrix instruction both GEMMs are built from
+ * (v_mfma_scale_f32_16x16x128_f8f6f4 with an MXFP4 A and an FP8 B operand),
+ * once per 16 x 16 tile, from a zero accumulator; exported so that its
+ * operand layout, scale-byte selection and accumulation error can be
+ * measured against exact arithmetic (the local error budget of the
+ * requantised intermediate rests on that error).  For tile i < n:
+ *   a_fp4   [n, 16, 64]   E2M1 codes of rows m, K = 128 (element 2c low nibble)
+ *   a_scale [n, 16, 4]    E8M0 scale of row m's K block of 32
+ *   b_fp8   [n, 16, 128]  E4M3 codes of columns c
+ *   b_scale [n, 16, 4]    E8M0 scale of column c's K block of 32
+ *   d       [n, 16, 16]   float32 out: sum over K of the scaled products
+ * byte_sel (0..3) is the byte of its 32-bit operand that carries A's scale
+ * (the other bytes hold an invalid code).  Limits: 0 <= n <= 2^24. */
+int moe_a8w4_mfma_probe(int64_t n, int32_t byte_sel, const uint8_t* a_fp4, const uint8_t* a_scale,
+                        const uint8_t* b_fp8, const uint8_t* b_scale, float* d, hipStream_t stream);
 
 /* Name of a status code (static string). */
 const char* moe_a8w4_status_str(int status);

@@ -30,6 +30,7 @@ EXPORTS = (
     "moe_a8w4_stage1", "moe_a8w4_stage2", "moe_a8w4_combine", "moe_a8w4_status_str",
     "moe_a8w4_route", "moe_a8w4_forward_routed", "moe_a8w4_stages_fused", "moe_a8w4_fused_counters",
     "moe_a16w4_forward", "moe_a16w4_workspace_bytes", "moe_a16w4_block_m", "moe_a16w4_stage1",
+    "moe_a8w4_mfma_probe",
 )
 
 
@@ -83,6 +84,7 @@ def load() -> ctypes.CDLL:
         "moe_a16w4_workspace_bytes": (ctypes.c_int, [P, ctypes.POINTER(sz)]),
         "moe_a16w4_block_m": (ctypes.c_int, [P]),
         "moe_a16w4_stage1": (ctypes.c_int, [P, i32] + [vp] * 7 + [vp]),
+        "moe_a8w4_mfma_probe": (ctypes.c_int, [ctypes.c_int64, i32] + [vp] * 5 + [vp]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -355,3 +357,15 @@ def moe_a8w4_combine(dims, topk_ids, y_routes, out=None, stream=None):
                                  _stream(stream))
     _check("moe_a8w4_combine", st)
     return out
+
+
+def moe_a8w4_mfma_probe(a_fp4, a_scale, b_fp8, b_scale, byte_sel=0, d=None, stream=None):
+    """n scaled MFMAs: a_fp4 [n,16,64], a_scale [n,16,4], b_fp8 [n,16,128],
+    b_scale [n,16,4] uint8 -> d float32 [n,16,16]."""
+    n = a_fp4.shape[0]
+    if d is None:
+        d = torch.empty((n, 16, 16), dtype=torch.float32, device=a_fp4.device)
+    st = load().moe_a8w4_mfma_probe(n, byte_sel, _ptr(a_fp4), _ptr(a_scale), _ptr(b_fp8), _ptr(b_scale),
+                                    _ptr(d), _stream(stream))
+    _check("moe_a8w4_mfma_probe", st)
+    return d

@@ -9,7 +9,8 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libmoe_a8w4.so")
-SOURCES = ["api.hip", "elementwise.hip", "sort.hip", "gemm.hip", "gemm_tile.hip", "gemm_a16.hip"]
+SOURCES = ["api.hip", "elementwise.hip", "sort.hip", "gemm.hip", "gemm_tile.hip", "gemm_a16.hip",
+           "probe.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 FLAGS = [

@@ -4,6 +4,8 @@
 #include <stdint.h>
 #include <stddef.h>
 
+#include <initializer_list>
+
 #include "moe_a8w4.h"
 #include "common.hpp"
 #include "launch.hpp"
@@ -24,6 +26,14 @@ int check_dims(const moe_a8w4_dims* d) {
 }
 
 bool aligned(const void* p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
+
+// Every pointer of a call 16-byte aligned, as the header requires (kernels
+// read ids, codes and scales with 16-byte loads).
+bool all_aligned16(std::initializer_list<const void*> ps) {
+  for (const void* p : ps)
+    if (!aligned(p, 16)) return false;
+  return true;
+}
 
 int status_of(hipError_t e) { return e == hipSuccess ? MOE_OK : (int)e; }
 
@@ -314,7 +324,7 @@ int moe_a8w4_quant_act(int32_t M, int32_t H, const void* x, uint8_t* q, uint8_t*
   if (M < 0 || H <= 0 || H % 32 != 0) return MOE_ERR_DIMS;
   if (M == 0) return MOE_OK;
   if (!x || !q || !s) return MOE_ERR_NULL;
-  if (!aligned(x, 16) || !aligned(q, 16)) return MOE_ERR_ALIGN;
+  if (!all_aligned16({x, q, s})) return MOE_ERR_ALIGN;
   return status_of(moe::launch_prep(nullptr, M, 1, 1, 0, 16, nullptr, nullptr, nullptr,
                                      static_cast<const uint16_t*>(x), H, q, s, moe::RouteArgs{}, stream));
 }
@@ -327,6 +337,7 @@ int moe_a8w4_sort(const moe_a8w4_dims* dims, int32_t block_m, const int32_t* top
   if (!valid_bm(block_m)) return MOE_ERR_BLOCK_M;
   if (!num_padded) return MOE_ERR_NULL;
   if (dims->tokens > 0 && (!topk_ids || !sorted_ids || !block_expert)) return MOE_ERR_NULL;
+  if (!all_aligned16({topk_ids, sorted_ids, block_expert, num_padded})) return MOE_ERR_ALIGN;
   return status_of(moe::launch_prep(topk_ids, dims->tokens, dims->topk, dims->num_experts,
                                     dims->expert_offset, block_m, sorted_ids, block_expert,
                                     num_padded, nullptr, 0, nullptr, nullptr, moe::RouteArgs{}, stream));
@@ -342,7 +353,7 @@ int moe_a8w4_quant_sort(const moe_a8w4_dims* dims, int32_t block_m, const void* 
   const void* ptrs[7] = {hidden, topk_ids, a_q, a_s, sorted_ids, block_expert, num_padded};
   for (const void* p : ptrs)
     if (!p) return MOE_ERR_NULL;
-  if (!aligned(hidden, 16) || !aligned(a_q, 16)) return MOE_ERR_ALIGN;
+  if (!all_aligned16({hidden, topk_ids, a_q, a_s, sorted_ids, block_expert, num_padded})) return MOE_ERR_ALIGN;
   return status_of(moe::launch_prep(topk_ids, dims->tokens, dims->topk, dims->num_experts,
                                     dims->expert_offset, block_m, sorted_ids, block_expert,
                                     num_padded, static_cast<const uint16_t*>(hidden), dims->hidden,
@@ -360,8 +371,7 @@ int moe_a8w4_stage1(const moe_a8w4_dims* dims, int32_t block_m, const uint8_t* a
   const void* ptrs[9] = {a_q, a_s, sorted_ids, block_expert, num_padded, w13_p, w13_s_p, inter_q, inter_s};
   for (const void* p : ptrs)
     if (!p) return MOE_ERR_NULL;
-  if (!aligned(a_q, 16) || !aligned(w13_p, 16) || !aligned(w13_s_p, 16) || !aligned(inter_q, 16) ||
-      !aligned(a_s, 4))
+  if (!all_aligned16({a_q, a_s, sorted_ids, block_expert, num_padded, w13_p, w13_s_p, inter_q, inter_s}))
     return MOE_ERR_ALIGN;
   const int64_t max_blocks = capacity(dims, block_m) / block_m;
   return status_of(moe::launch_stage1(stage1_args(dims, block_m, a_q, a_s, sorted_ids, block_expert,
@@ -381,8 +391,8 @@ int moe_a8w4_stage2(const moe_a8w4_dims* dims, int32_t block_m, const uint8_t* i
                           w2_p, w2_s_p, y_routes, inter_q};
   for (const void* p : ptrs)
     if (!p) return MOE_ERR_NULL;
-  if (!aligned(inter_q, 16) || !aligned(w2_p, 16) || !aligned(w2_s_p, 16) || !aligned(y_routes, 16) ||
-      !aligned(inter_s, 4))
+  if (!all_aligned16({inter_q, inter_s, sorted_ids, block_expert, num_padded, topk_weights, w2_p, w2_s_p,
+                      y_routes}))
     return MOE_ERR_ALIGN;
   const int64_t max_blocks = capacity(dims, block_m) / block_m;
   return status_of(moe::launch_stage2(stage2_args(dims, block_m, inter_q, inter_s, sorted_ids,
@@ -397,7 +407,7 @@ int moe_a8w4_combine(const moe_a8w4_dims* dims, const int32_t* topk_ids, const v
   if (st) return st;
   if (dims->tokens == 0) return MOE_OK;
   if (!topk_ids || !y_routes || !out) return MOE_ERR_NULL;
-  if (!aligned(y_routes, 16) || !aligned(out, 16)) return MOE_ERR_ALIGN;
+  if (!all_aligned16({topk_ids, y_routes, out})) return MOE_ERR_ALIGN;
   return status_of(moe::launch_combine(dims->tokens, dims->hidden, dims->topk, dims->num_experts,
                                        dims->expert_offset, topk_ids,
                                        static_cast<const int16_t*>(y_routes),
@@ -426,10 +436,9 @@ int moe_a8w4_stages_fused(const moe_a8w4_dims* dims, int32_t block_m, const uint
                           w13_s_p, w2_p, w2_s_p, inter_q, inter_s, y_routes, counters, out, a_q};
   for (const void* p : ptrs)
     if (!p) return MOE_ERR_NULL;
-  const void* al[8] = {a_q, w13_p, w13_s_p, w2_p, w2_s_p, inter_q, y_routes, out};
-  for (const void* p : al)
-    if (!aligned(p, 16)) return MOE_ERR_ALIGN;
-  if (!aligned(counters, 4) || !aligned(a_s, 4) || !aligned(inter_s, 4)) return MOE_ERR_ALIGN;
+  if (!all_aligned16({a_q, a_s, sorted_ids, block_expert, num_padded, topk_ids, topk_weights, w13_p, w13_s_p,
+                      w2_p, w2_s_p, inter_q, inter_s, y_routes, counters, out}))
+    return MOE_ERR_ALIGN;
   const int64_t max_blocks = capacity(dims, block_m) / block_m;
   return status_of(moe::launch_fused(
       stage1_args(dims, block_m, a_q, a_s, sorted_ids, block_expert, num_padded, w13_p, w13_s_p, inter_q,
@@ -465,7 +474,7 @@ int moe_a16w4_stage1(const moe_a8w4_dims* dims, int32_t block_m, const void* hid
   const void* ptrs[7] = {hidden, sorted_ids, block_expert, num_padded, w13_p, w13_s_p, inter_bf16};
   for (const void* p : ptrs)
     if (!p) return MOE_ERR_NULL;
-  if (!aligned(hidden, 16) || !aligned(w13_p, 16) || !aligned(w13_s_p, 16) || !aligned(inter_bf16, 16))
+  if (!all_aligned16({hidden, sorted_ids, block_expert, num_padded, w13_p, w13_s_p, inter_bf16}))
     return MOE_ERR_ALIGN;
   return status_of(moe::launch_a16_stage1(
       a16_stage1_args(dims, block_m, hidden, sorted_ids, block_expert, num_padded, w13_p, w13_s_p, inter_bf16),
@@ -510,6 +519,15 @@ int moe_a16w4_forward(const moe_a8w4_dims* dims, const void* hidden, const int32
   return status_of(moe::launch_combine(dims->tokens, dims->hidden, dims->topk, dims->num_experts,
                                        dims->expert_offset, topk_ids, reinterpret_cast<int16_t*>(y),
                                        y + route_codes_bytes(dims), static_cast<uint16_t*>(out), stream));
+}
+
+int moe_a8w4_mfma_probe(int64_t n, int32_t byte_sel, const uint8_t* a_fp4, const uint8_t* a_scale,
+                        const uint8_t* b_fp8, const uint8_t* b_scale, float* d, hipStream_t stream) {
+  if (n < 0 || n > (1 << 24) || byte_sel < 0 || byte_sel > 3) return MOE_ERR_DIMS;
+  if (n == 0) return MOE_OK;
+  if (!a_fp4 || !a_scale || !b_fp8 || !b_scale || !d) return MOE_ERR_NULL;
+  if (!aligned(a_fp4, 16) || !aligned(b_fp8, 16) || !aligned(d, 4)) return MOE_ERR_ALIGN;
+  return status_of(moe::launch_mfma_probe(n, byte_sel, a_fp4, a_scale, b_fp8, b_scale, d, stream));
 }
 
 const char* moe_a8w4_status_str(int status) {

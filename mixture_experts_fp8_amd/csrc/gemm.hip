@@ -6,12 +6,9 @@
 // tokens' FP8 activations, SiLU(gate) * up, and per-1x32 FP8 requantisation of
 // the intermediate, with no routing weight.  Stage two: w2[e] times that
 // intermediate, scaled by the routing weight, written per route (token, slot)
-// for the top-k combine.  (aiter PR 5609, "Add DeepSeek V4.1 Flash TP4 gfx950 MoE
-// tuning", Configuration: BF16 output, FP8 activations, MXFP4 weights,
-// per-1x32 scaling, interleaved gate/up, SiLU, no stage-one routing-weight
-// multiplication; aiter PR 5904, "Fused-MoE kernel, expert-parallel
-// benchmark": sorting, both stages and the intermediate quantization form one
-// call.)
+// for the top-k combine.  (The layer's definition: aiter PR 5609, "Add
+// DeepSeek V4.1 Flash TP4 gfx950 MoE tuning", Configuration; the span of one
+// call: aiter PR 5904, "Fused-MoE kernel, expert-parallel benchmark".)
 //
 // Mapping ("swap-AB"): the weight rows are the MFMA's A matrix (16 rows x 128 K
 // of FP4 per instruction, read straight from the packed weight layout, 4 KB

@@ -84,5 +84,8 @@ hipError_t launch_a16_stage2(const GemmArgs& a, int64_t max_blocks, hipStream_t 
 hipError_t launch_a16_tile(int stage, const GemmArgs& a, int64_t max_blocks, hipStream_t stream);
 // LDS-tiled variant of either stage for bm = 64 or 128 (gemm_tile.hip)
 hipError_t launch_tile(int stage, const GemmArgs& a, int64_t max_blocks, hipStream_t stream);
+// n independent 16 x 16 scaled MFMAs, A scale as byte sel of its operand (probe.hip)
+hipError_t launch_mfma_probe(int64_t n, int sel, const uint8_t* a, const uint8_t* as, const uint8_t* b,
+                             const uint8_t* bs, float* d, hipStream_t stream);
 
 }  // namespace moe

@@ -1,0 +1,60 @@
+// The scaled MFMA the grouped GEMMs are built from, one instruction per
+// 16 x 16 output tile, exported so that tests can measure it against exact
+// arithmetic: its operand layout, its scale-byte selection and the error of
+// its internal accumulation (which sets the local error budget of the
+// requantised intermediate).
+#include "gemm_common.hpp"
+
+namespace moe {
+
+namespace {
+
+// One wave per tile i:
+//   A  [16 rows][64 bytes]  E2M1 codes, K = 128, element 2c in the low nibble
+//   as [16 rows][4]         E8M0 scale of each row's K blocks of 32
+//   B  [16 cols][128 bytes] E4M3 codes
+//   bs [16 cols][4]         E8M0 scale of each column's K blocks of 32
+//   D  [16 rows][16 cols]   float32, from a zero accumulator
+// The scale bytes reach the instruction as byte SEL of their 32-bit operand
+// (the other bytes hold 0xFF, an invalid scale); the B scale is byte 0 of its
+// operand, the others 0xFF likewise.  So the byte selection is checked too.
+template <int SEL>
+__global__ void __launch_bounds__(64) mfma_probe_kernel(const uint8_t* __restrict__ a,
+                                                        const uint8_t* __restrict__ as,
+                                                        const uint8_t* __restrict__ b,
+                                                        const uint8_t* __restrict__ bs,
+                                                        float* __restrict__ d) {
+  const int64_t i = blockIdx.x;
+  const int lane = threadIdx.x, m = lane & 15, g = lane >> 4;
+  const uint8_t* ai = a + i * 16 * 64;
+  const uint8_t* bi = b + i * 16 * 128;
+  // A lane (m, g): row m, K [32 g, +32) = 16 bytes at 16 g
+  const v4i av = *reinterpret_cast<const v4i*>(ai + m * 64 + 16 * g);
+  // B lane (n, g): column n, K [16 g, +16) and [64 + 16 g, +16)
+  const v4i b0 = *reinterpret_cast<const v4i*>(bi + m * 128 + 16 * g);
+  const v4i b1 = *reinterpret_cast<const v4i*>(bi + m * 128 + 64 + 16 * g);
+  // scale of lane group g: K block g of row / column m
+  const uint32_t sa = (0xFFFFFFFFu & ~(0xFFu << (8 * SEL))) | ((uint32_t)as[i * 64 + m * 4 + g] << (8 * SEL));
+  const uint32_t sb = 0xFFFFFF00u | (uint32_t)bs[i * 64 + m * 4 + g];
+  const v4f acc = mfma_fp4_fp8<SEL>(av, join8(b0, b1), v4f{0.f, 0.f, 0.f, 0.f}, sa, sb);
+  // D lane (n, g): column n, rows 4 g .. 4 g + 3
+#pragma unroll
+  for (int r = 0; r < 4; ++r) d[i * 256 + (4 * g + r) * 16 + m] = acc[r];
+}
+
+}  // namespace
+
+hipError_t launch_mfma_probe(int64_t n, int sel, const uint8_t* a, const uint8_t* as, const uint8_t* b,
+                             const uint8_t* bs, float* d, hipStream_t stream) {
+  if (n <= 0) return hipSuccess;
+  const dim3 grid((unsigned)n), blk(64);
+  switch (sel) {
+    case 0: hipLaunchKernelGGL(mfma_probe_kernel<0>, grid, blk, 0, stream, a, as, b, bs, d); break;
+    case 1: hipLaunchKernelGGL(mfma_probe_kernel<1>, grid, blk, 0, stream, a, as, b, bs, d); break;
+    case 2: hipLaunchKernelGGL(mfma_probe_kernel<2>, grid, blk, 0, stream, a, as, b, bs, d); break;
+    default: hipLaunchKernelGGL(mfma_probe_kernel<3>, grid, blk, 0, stream, a, as, b, bs, d); break;
+  }
+  return hipGetLastError();
+}
+
+}  // namespace moe

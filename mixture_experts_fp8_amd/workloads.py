@@ -21,8 +21,10 @@ the workloads the pages measure:
 Distributions (no trained weights exist here, so all are synthetic):
   weights  E2M1 codes uniform over the 16 codes, E8M0 scale codes uniform over
            {119, 120, 121, 122} (block exponents -8 ... -5); intermediate
-           columns past the valid width hold code 0.
-  hidden   BF16 of N(0, 1) draws.
+           columns past the valid width hold code 0.  (The numerical stress
+           geometry "wide-scale" draws codes 100 ... 140 instead.)
+  hidden   BF16 of N(0, 1) draws (in "wide-scale" each block of 32 scaled by
+           a power of two between 2^-20 and 2^20).
   routing  softmax of N(0, 1) logits, top-k, renormalised to sum 1 (float32);
            concentrated: 80 % of a token's slots go to 4 hot experts;
            round-robin: ids (t*k + s) mod E with weights 1/k;
@@ -56,6 +58,8 @@ class Workload:
     tokens: tuple        # token counts (M) of the workload
     routings: tuple      # routing modes exercised
     config_id: int
+    scale_codes: tuple = None   # E8M0 weight scale codes drawn (None: WEIGHT_SCALE_CODES)
+    act_exp_spread: int = 0     # hidden blocks of 32 scaled by 2^u, u uniform in [-spread, spread]
 
 
 WORKLOADS = {
@@ -75,6 +79,12 @@ WORKLOADS = {
                                (12, 256, 1024, 1536, 4096, 16384), ("roundrobin",), 6),
     "a16w4-shared": Workload("a16w4-shared", 5120, 768, 768, 385, 384, 7, True, 0,
                              (12, 256, 1024, 1536, 4096, 16384), ("roundrobin",), 7),
+    # a numerical stress geometry, not a measured one: weight scales over 41
+    # binades (codes 100 ... 140) and hidden blocks scaled by 2^-20 ... 2^20,
+    # so the MFMA scale operands and the requantisation exponents span a wide
+    # range (the measured workloads keep them within a few binades)
+    "wide-scale": Workload("wide-scale", 5120, 640, 576, 32, 32, 4, False, 0,
+                           (40, 300, 1100), ("softmax",), 8, scale_codes=(100, 140), act_exp_spread=20),
 }
 
 # the decode buckets of the backbone geometry (the boundary counts are parity cases)
@@ -101,7 +111,8 @@ def make_weights(w: Workload, seed=None):
     """(w13 [E,2I,H/2], w13_s [E,2I,H/32], w2 [E,H,I/2], w2_s [E,H,I/32]) as uint8."""
     rng = np.random.default_rng([w.config_id, 1] if seed is None else seed)
     E, H, I, Iv = w.num_experts, w.hidden, w.inter, w.inter_valid
-    lo, hi = WEIGHT_SCALE_CODES[0], WEIGHT_SCALE_CODES[-1] + 1
+    sc = WEIGHT_SCALE_CODES if w.scale_codes is None else w.scale_codes
+    lo, hi = sc[0], sc[-1] + 1
 
     def codes(shape):  # uniform random bytes = two independent uniform E2M1 codes
         n = int(np.prod(shape))
@@ -123,8 +134,13 @@ def cached_weights(w: Workload):
     return make_weights(w)
 
 
-def make_hidden(rng, M: int, H: int) -> np.ndarray:
-    return bf16_bits(rng.standard_normal((M, H), dtype=np.float32))
+def make_hidden(rng, M: int, H: int, exp_spread: int = 0) -> np.ndarray:
+    x = rng.standard_normal((M, H), dtype=np.float32)
+    if exp_spread:
+        # one power of two per block of 32: exact in BF16, no overflow
+        e = rng.integers(-exp_spread, exp_spread + 1, size=(M, H // 32))
+        x = x * np.repeat(np.exp2(e).astype(np.float32), 32, axis=1)
+    return bf16_bits(x)
 
 
 def _softmax_topk(logits: np.ndarray, k: int):
@@ -182,7 +198,7 @@ def make_routing(rng, w: Workload, M: int, mode: str):
 def make_inputs(w: Workload, M: int, mode: str = "softmax", seed=None):
     """(hidden BF16 bits [M,H], topk_ids [M,k], topk_weights [M,k]) for one call."""
     rng = np.random.default_rng([w.config_id, 2, M, ROUTINGS.index(mode)] if seed is None else seed)
-    hidden = make_hidden(rng, M, w.hidden)
+    hidden = make_hidden(rng, M, w.hidden, w.act_exp_spread)
     ids, wts = make_routing(rng, w, M, mode)
     return hidden, ids, wts
 

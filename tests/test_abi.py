@@ -190,3 +190,46 @@ def test_fused_launch_entry_points_validate():
         assert lib.moe_a8w4_stages_fused(ctypes.byref(d), 16, *ptrs, None) == abi.MOE_ERR_NULL
     z = dims(tokens=0)
     assert lib.moe_a8w4_stages_fused(ctypes.byref(z), 16, *([None] * 16), None) == abi.MOE_OK
+
+
+@pytest.mark.parametrize("which", range(16))
+def test_step_entry_points_reject_each_misaligned_pointer(which):
+    """Every pointer of the step entry points must be 16-byte aligned (the
+    kernels read ids, codes and scales with 16-byte loads): one pointer at a
+    4- or 24-byte offset gives MOE_ERR_ALIGN before any launch."""
+    lib = abi.load()
+    d = dims()
+    ok = 1 << 20
+
+    def ptrs(n):
+        ps = [ctypes.c_void_p(ok + 4096 * i) for i in range(n)]
+        if which < n:
+            ps[which] = ctypes.c_void_p(ok + 4096 * which + (24 if which % 2 else 4))
+        return ps
+
+    calls = {
+        "sort": lambda: lib.moe_a8w4_sort(ctypes.byref(d), 16, *ptrs(4), None),
+        "quant_sort": lambda: lib.moe_a8w4_quant_sort(ctypes.byref(d), 16, *ptrs(7), None),
+        "stage1": lambda: lib.moe_a8w4_stage1(ctypes.byref(d), 16, *ptrs(9), None),
+        "stage2": lambda: lib.moe_a8w4_stage2(ctypes.byref(d), 16, *ptrs(9), None),
+        "combine": lambda: lib.moe_a8w4_combine(ctypes.byref(d), *ptrs(3), None),
+        "quant_act": lambda: lib.moe_a8w4_quant_act(4, 512, *ptrs(3), None),
+        "stages_fused": lambda: lib.moe_a8w4_stages_fused(ctypes.byref(d), 16, *ptrs(16), None),
+        "a16_stage1": lambda: lib.moe_a16w4_stage1(ctypes.byref(d), 16, *ptrs(7), None),
+        "forward": lambda: lib.moe_a8w4_forward(ctypes.byref(d), *ptrs(9), 1 << 40, None),
+    }
+    nptr = {"sort": 4, "quant_sort": 7, "stage1": 9, "stage2": 9, "combine": 3, "quant_act": 3,
+            "stages_fused": 16, "a16_stage1": 7, "forward": 9}
+    for name, call in calls.items():
+        if which < nptr[name]:
+            assert call() == abi.MOE_ERR_ALIGN, (name, which)
+
+
+def test_mfma_probe_validates():
+    lib = abi.load()
+    p = ctypes.c_void_p(1 << 20)
+    assert lib.moe_a8w4_mfma_probe(0, 0, None, None, None, None, None, None) == abi.MOE_OK
+    assert lib.moe_a8w4_mfma_probe(1, 4, p, p, p, p, p, None) == abi.MOE_ERR_DIMS
+    assert lib.moe_a8w4_mfma_probe(-1, 0, p, p, p, p, p, None) == abi.MOE_ERR_DIMS
+    assert lib.moe_a8w4_mfma_probe(1, 0, p, None, p, p, p, None) == abi.MOE_ERR_NULL
+    assert lib.moe_a8w4_mfma_probe(1, 0, ctypes.c_void_p((1 << 20) + 8), p, p, p, p, None) == abi.MOE_ERR_ALIGN

@@ -1,13 +1,15 @@
 """GPU parity of the whole layer through the C ABI against the oracle, at the
-gate of the pages' validation (atol = rtol = 2e-2, all outputs finite):
-small geometries on every token, the five workloads at full size on sampled
-tokens, edge cases, input preservation, the step entry points, and replays
-of a captured graph on changed inputs."""
+gate of the pages' validation (atol = rtol = 2e-2, all outputs finite), on
+every token: small geometries, every point of the five workloads at full size
+(with the pages' boundary token counts), a numerical stress geometry, edge
+cases, input preservation, the step entry points, and replays of a captured
+graph on changed inputs."""
 import numpy as np
 import pytest
 import torch
 
 from mixture_experts_fp8_amd import abi, workloads as wl
+import oracle
 from gpu_util import DEV, Layer, assert_gate, check_forward, dev, host_bf16_bits, note
 
 pytestmark = pytest.mark.gpu
@@ -43,11 +45,23 @@ def test_forward_small_all_tokens(name, E, M, mode):
     check_forward(layer, hidden, ids, wts, host_bf16_bits(out), xd, idd)
 
 
-FULL = [("draft-decode", 5, "softmax"), ("backbone-decode", 768, "softmax"),
-        ("backbone-decode", 256, "softmax"), ("draft-sweep", 640, "concentrated"),
-        ("local-slice", 1024, "softmax"), ("local-slice", 4096, "softmax"),
-        ("local-slice", 16384, "softmax"),
-        ("prefill-shared", 4096, "roundrobin"), ("prefill-shared", 16384, "softmax")]
+# Every point of the five workloads, each token checked against the oracle:
+# the draft decode call; the backbone decode buckets and the boundary token
+# counts of the pages' validation (aiter PR 5609, "Validation and limits":
+# M 31/32/33/255/256/257 in each geometry); the draft sweep under both
+# routings plus the boundary counts; the local-slice token counts of the
+# pages' benchmark table (aiter PR 5904, "Fused-MoE kernel, expert-parallel
+# benchmark") plus the boundary counts; the prefill geometry with the shared
+# expert under both routings; and the numerical stress geometry.
+BOUNDARY = (31, 32, 33, 255, 256, 257)
+FULL = ([("draft-decode", 5, "softmax")]
+        + [("backbone-decode", M, "softmax") for M in wl.BACKBONE_DECODE_BUCKETS + BOUNDARY]
+        + [("draft-sweep", M, mode) for mode in ("softmax", "concentrated")
+           for M in wl.WORKLOADS["draft-sweep"].tokens]
+        + [("draft-sweep", M, "softmax") for M in BOUNDARY]
+        + [("local-slice", M, "softmax") for M in wl.WORKLOADS["local-slice"].tokens + BOUNDARY]
+        + [("prefill-shared", M, mode) for M in (4096, 16384) for mode in ("roundrobin", "softmax")]
+        + [("wide-scale", M, "softmax") for M in wl.WORKLOADS["wide-scale"].tokens])
 
 
 @pytest.fixture(scope="module")
@@ -66,7 +80,7 @@ def layers():
 
 
 @pytest.mark.parametrize("name,M,mode", FULL)
-def test_forward_full_size_sampled(layers, name, M, mode):
+def test_forward_full_size_every_token(layers, name, M, mode):
     layer = layers(name)
     w = layer.w
     hidden, ids, wts = wl.make_inputs(w, M, mode)
@@ -82,11 +96,19 @@ def test_forward_full_size_sampled(layers, name, M, mode):
     le = ids.astype(np.int64) - w.expert_offset
     none_local = ~((le >= 0) & (le < w.num_experts)).any(axis=1)
     assert np.all(vals[none_local] == 0)
-    # sampled rows against the oracle: first, last and random ones
-    rng = np.random.default_rng(M)
-    n = 4 if M >= 4096 else 6
-    tok = np.unique(np.concatenate([[0, M - 1], rng.integers(0, M, n)])).astype(np.int64)
-    check_forward(layer, hidden, ids, wts, bits, xd, idd, tokens=tok)
+    # the sort at full size, bit for bit
+    d = layer.dims(M)
+    bm = abi.moe_a8w4_block_m(d)
+    srt, bexp, npad = abi.moe_a8w4_sort(d, bm, idd)
+    torch.cuda.synchronize()
+    ref_sorted, ref_bexp = oracle.sort(ids, w.num_experts, w.expert_offset, bm)
+    P = int(npad.item())
+    assert P == len(ref_sorted)
+    assert np.array_equal(srt[:P].cpu().numpy(), ref_sorted)
+    assert np.array_equal(bexp[:P // bm].cpu().numpy(), ref_bexp)
+    # every token against the oracle (the stress geometry's outputs reach
+    # 2^90 with heavy cancellation: stage two is held to its own budget there)
+    check_forward(layer, hidden, ids, wts, bits, xd, idd, stage2_within_budget=(name == "wide-scale"))
     # inputs unchanged
     assert np.array_equal(host_bf16_bits(xd), hidden)
     assert np.array_equal(idd.cpu().numpy(), ids)

@@ -1,17 +1,19 @@
-"""GPU checks of the fused decode launch (stage one, stage two and the top-k
-combine in one kernel, blocks of 16 or 32 routes).  It runs the same tile
-arithmetic as the separate stage launches, so its intermediate, its route rows
-and its output must equal theirs bit for bit; the separate launches are
-checked against the oracle in test_gpu_steps.py, and the layer (which takes
-the fused launch at these sizes) in test_gpu_forward.py.  Also: its
-cross-workgroup counters are left zero and its status word 0 after every call,
-so back-to-back calls on one counters buffer stay correct."""
+"""GPU checks of the fused decode launch moe_a8w4_stages_fused (stage one,
+stage two and the top-k combine in one kernel, blocks of 16 or 32 routes),
+an export beside moe_a8w4_forward (which runs separate launches).  It runs
+the same tile arithmetic as the separate stage launches, so its
+intermediate, its route rows and its output must equal theirs bit for bit;
+its output is also checked against the oracle on every token (the gate of
+the pages' validation, with the two-part check of gpu_util.check_forward on
+the fused launch's own intermediate).  Its cross-workgroup counters are left
+zero and its status word 0 after every call, so back-to-back calls on one
+counters buffer stay correct."""
 import numpy as np
 import pytest
 import torch
 
 from mixture_experts_fp8_amd import abi, workloads as wl
-from gpu_util import DEV, Layer, dev, note
+from gpu_util import DEV, Layer, check_forward, dev, host_bf16_bits, note
 
 pytestmark = pytest.mark.gpu
 
@@ -80,10 +82,14 @@ def test_fused_equals_separate_launches(name, E, routed, M, mode):
         assert not counters.any(), "rep %d: counters not cleared: status %d, %d nonzero" % (
             rep, int(counters[0]), int((counters != 0).sum()))
         compare(d, bm, ref, iq, is_, y, out, ids, w.num_experts, w.expert_offset)
-        # and the whole layer through moe_a8w4_forward (the same fused launch)
+        # the whole layer through moe_a8w4_forward: the same output
         fwd = layer.forward(xd, idd, wd)
         torch.cuda.synchronize()
-        assert torch.equal(fwd.view(torch.int16), ref[-1].view(torch.int16))
+        assert torch.equal(fwd.view(torch.int16), out.view(torch.int16))
+        # and the fused launch's output against the oracle, every token
+        P = int(npad.item())
+        inter = (srt[:P].cpu().numpy(), iq[:P].cpu().numpy(), is_[:P].cpu().numpy())
+        check_forward(layer, hidden, ids, wts, host_bf16_bits(out), xd, idd, inter=inter)
 
 
 FULL = [("backbone-decode", 6), ("backbone-decode", 768), ("local-slice", 1), ("local-slice", 256)]
@@ -107,8 +113,9 @@ def full_layers():
 
 @pytest.mark.parametrize("name,M", FULL)
 def test_fused_full_size(name, M, full_layers):
-    """The real geometries (384 experts at I 640; 96 local experts at I 2304),
-    fused launch against the separate launches, bit for bit."""
+    """The real geometries (384 experts at I 640; 96 local experts at I 2304):
+    the fused launch against the separate launches, bit for bit, and against
+    the oracle on every token."""
     w = wl.WORKLOADS[name]
     layer = full_layers(name)
     hidden, ids, wts = wl.make_inputs(w, M, w.routings[0])
@@ -124,3 +131,6 @@ def test_fused_full_size(name, M, full_layers):
     torch.cuda.synchronize()
     assert not counters.any()
     compare(d, bm, ref, iq, is_, y, out, ids, w.num_experts, w.expert_offset)
+    P = int(npad.item())
+    inter = (srt[:P].cpu().numpy(), iq[:P].cpu().numpy(), is_[:P].cpu().numpy())
+    check_forward(layer, hidden, ids, wts, host_bf16_bits(out), xd, idd, inter=inter)

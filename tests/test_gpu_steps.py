@@ -7,7 +7,7 @@ import torch
 
 import oracle
 from mixture_experts_fp8_amd import abi, workloads as wl
-from gpu_util import DEV, Layer, _E4M3, check_intermediate, dev, note
+from gpu_util import DEV, Layer, _E4M3, check_routes_intermediate, dev, note
 
 pytestmark = pytest.mark.gpu
 
@@ -148,7 +148,7 @@ def test_stage1_intermediate(name, M, E):
     """Stage one against the oracle's requantised intermediate, route by route.
 
     The GPU intermediate must be a faithful rounding of the oracle's exact
-    value (see gpu_util.check_intermediate), and rows holding a route must be
+    value (see gpu_util.check_routes_intermediate), and rows holding a route must be
     fully written: the buffers start as 0xFF, which no code or scale takes.
     """
     w = wl.scaled(wl.WORKLOADS[name], num_experts=E, routed_experts=E, config_id=60 + E)
@@ -172,7 +172,7 @@ def test_stage1_intermediate(name, M, E):
     gis = is_.cpu().numpy()[real]
     assert not (gis == 0xFF).any(), "unwritten scales in routed rows"
     assert not (giq == 0xFF).any(), "unwritten codes in routed rows"
-    check_intermediate(L, hidden, ids, routes, giq, gis)
+    check_routes_intermediate(L, hidden, ids, routes, giq, gis)
     if w.inter_valid < w.inter:
         assert np.all((giq[:, w.inter_valid:] & 0x7F) == 0)
 
