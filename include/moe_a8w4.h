@@ -59,6 +59,11 @@ extern "C" {
 #define MOE_ERR_ALIGN (-3)     /* a pointer is not 16-byte (workspace: 256-byte) aligned */
 #define MOE_ERR_WORKSPACE (-4) /* workspace_bytes smaller than moe_a8w4_workspace_bytes() */
 #define MOE_ERR_BLOCK_M (-5)   /* block_m not one of 16, 32, 64, 128 */
+#define MOE_ERR_SCRATCH (-6)   /* moe_a8w4_forward_noalloc: the call needs more than
+                                  MOE_A8W4_NOALLOC_SCRATCH_BYTES of workspace */
+
+/* Size of the static device scratch of moe_a8w4_forward_noalloc (per GPU). */
+#define MOE_A8W4_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
 
 typedef struct moe_a8w4_dims {
   int32_t tokens;        /* M: token rows in hidden / out / topk_* */
@@ -134,6 +139,22 @@ int moe_a8w4_forward(const moe_a8w4_dims* dims, const void* hidden, const int32_
                      const float* topk_weights, const uint8_t* w13_p, const uint8_t* w13_s_p,
                      const uint8_t* w2_p, const uint8_t* w2_s_p, void* out, void* workspace,
                      size_t workspace_bytes, hipStream_t stream);
+
+/* For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid allocation):
+ * moe_a8w4_forward with no workspace argument.  Its workspace is a static
+ * array of MOE_A8W4_NOALLOC_SCRATCH_BYTES (64 MiB) in device memory, one per
+ * GPU the library runs on, held until the process ends; the call allocates
+ * nothing (its first call on a device looks up that device's array).  Calls
+ * whose moe_a8w4_workspace_bytes() exceeds that size return MOE_ERR_SCRATCH
+ * and enqueue nothing (64 MiB covers, e.g., 384 experts top-6 at I 640 up to
+ * 768 tokens).  Every call on a GPU shares its array: calls that overlap on
+ * one GPU (other streams, other host threads) race and give undefined
+ * results; calls on one stream are ordered and safe.  Other arguments,
+ * results and errors as moe_a8w4_forward. */
+int moe_a8w4_forward_noalloc(const moe_a8w4_dims* dims, const void* hidden, const int32_t* topk_ids,
+                             const float* topk_weights, const uint8_t* w13_p, const uint8_t* w13_s_p,
+                             const uint8_t* w2_p, const uint8_t* w2_s_p, void* out, hipStream_t stream);
 
 /* The whole layer from the router logits: moe_a8w4_route (with
  * routed_experts = dims->routed_experts, k_routed = dims->topk minus the

@@ -21,6 +21,8 @@ MOE_ERR_DIMS = -2
 MOE_ERR_ALIGN = -3
 MOE_ERR_WORKSPACE = -4
 MOE_ERR_BLOCK_M = -5
+MOE_ERR_SCRATCH = -6
+NOALLOC_SCRATCH_BYTES = 64 << 20
 
 # every symbol include/moe_a8w4.h declares
 EXPORTS = (
@@ -30,7 +32,7 @@ EXPORTS = (
     "moe_a8w4_stage1", "moe_a8w4_stage2", "moe_a8w4_combine", "moe_a8w4_status_str",
     "moe_a8w4_route", "moe_a8w4_forward_routed", "moe_a8w4_stages_fused", "moe_a8w4_fused_counters",
     "moe_a16w4_forward", "moe_a16w4_workspace_bytes", "moe_a16w4_block_m", "moe_a16w4_stage1",
-    "moe_a8w4_mfma_probe",
+    "moe_a8w4_mfma_probe", "moe_a8w4_forward_noalloc",
 )
 
 
@@ -85,6 +87,7 @@ def load() -> ctypes.CDLL:
         "moe_a16w4_block_m": (ctypes.c_int, [P]),
         "moe_a16w4_stage1": (ctypes.c_int, [P, i32] + [vp] * 7 + [vp]),
         "moe_a8w4_mfma_probe": (ctypes.c_int, [ctypes.c_int64, i32] + [vp] * 5 + [vp]),
+        "moe_a8w4_forward_noalloc": (ctypes.c_int, [P] + [vp] * 8 + [vp]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -159,6 +162,19 @@ def moe_a8w4_forward(dims, hidden, topk_ids, topk_weights, w13_p, w13_s_p, w2_p,
                                  _ptr(w13_p), _ptr(w13_s_p), _ptr(w2_p), _ptr(w2_s_p), _ptr(out),
                                  _ptr(workspace), workspace.numel(), _stream(stream))
     _check("moe_a8w4_forward", st)
+    return out
+
+
+def moe_a8w4_forward_noalloc(dims, hidden, topk_ids, topk_weights, w13_p, w13_s_p, w2_p, w2_s_p,
+                             out=None, stream=None):
+    """moe_a8w4_forward with the library's static device scratch as workspace
+    (out is allocated here if not given; the C entry point allocates nothing)."""
+    if out is None:
+        out = torch.empty((dims.tokens, dims.hidden), dtype=torch.bfloat16, device=hidden.device)
+    st = load().moe_a8w4_forward_noalloc(ctypes.byref(dims), _ptr(hidden), _ptr(topk_ids), _ptr(topk_weights),
+                                         _ptr(w13_p), _ptr(w13_s_p), _ptr(w2_p), _ptr(w2_s_p), _ptr(out),
+                                         _stream(stream))
+    _check("moe_a8w4_forward_noalloc", st)
     return out
 
 

@@ -5,6 +5,7 @@
 #include <stddef.h>
 
 #include <initializer_list>
+#include <mutex>
 
 #include "moe_a8w4.h"
 #include "common.hpp"
@@ -530,6 +531,65 @@ int moe_a8w4_mfma_probe(int64_t n, int32_t byte_sel, const uint8_t* a_fp4, const
   return status_of(moe::launch_mfma_probe(n, byte_sel, a_fp4, a_scale, b_fp8, b_scale, d, stream));
 }
 
+}  // extern "C"
+
+// ------------------------------------------------- the no-allocation form
+//
+// moe_a8w4_forward_noalloc takes its workspace from this array instead of a
+// caller buffer.  In host code `scratch` names a host-side stand-in, not the
+// device copy: its device address is looked up once per device (with that
+// device current) and only that address is passed to kernels.
+namespace {
+
+static __device__ __align__(256) uint8_t scratch[MOE_A8W4_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices];
+
+// Device address of the current device's scratch array.
+int current_scratch(void** p) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return status_of(e);
+  if (dev < 0 || dev >= kMaxDevices) return status_of(hipErrorInvalidDevice);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return status_of(e);
+    if (!ptr) return status_of(hipErrorInvalidSymbol);
+    g_scratch_ptr[dev] = ptr;
+  }
+  *p = g_scratch_ptr[dev];
+  return MOE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int moe_a8w4_forward_noalloc(const moe_a8w4_dims* dims, const void* hidden, const int32_t* topk_ids,
+                             const float* topk_weights, const uint8_t* w13_p, const uint8_t* w13_s_p,
+                             const uint8_t* w2_p, const uint8_t* w2_s_p, void* out, hipStream_t stream) {
+  int st = check_dims(dims);
+  if (st) return st;
+  if (dims->tokens == 0) return MOE_OK;
+  const void* ptrs[8] = {hidden, topk_ids, topk_weights, w13_p, w13_s_p, w2_p, w2_s_p, out};
+  for (const void* p : ptrs) {
+    if (!p) return MOE_ERR_NULL;
+    if (!aligned(p, 16)) return MOE_ERR_ALIGN;
+  }
+  // nothing of the workspace has to start at zero: every byte a call reads
+  // was written earlier in the same call
+  if (layout(dims, choose_bm(dims)).total > MOE_A8W4_NOALLOC_SCRATCH_BYTES) return MOE_ERR_SCRATCH;
+  void* ws = nullptr;
+  st = current_scratch(&ws);
+  if (st) return st;
+  return forward_body(dims, hidden, topk_ids, topk_weights, moe::RouteArgs{}, w13_p, w13_s_p, w2_p, w2_s_p, out,
+                      ws, MOE_A8W4_NOALLOC_SCRATCH_BYTES, stream);
+}
+
 const char* moe_a8w4_status_str(int status) {
   switch (status) {
     case MOE_OK: return "ok";
@@ -538,6 +598,7 @@ const char* moe_a8w4_status_str(int status) {
     case MOE_ERR_ALIGN: return "a pointer is misaligned (16 B; workspace 256 B)";
     case MOE_ERR_WORKSPACE: return "workspace smaller than moe_a8w4_workspace_bytes()";
     case MOE_ERR_BLOCK_M: return "block_m must be 16, 32, 64 or 128";
+    case MOE_ERR_SCRATCH: return "the call needs more than MOE_A8W4_NOALLOC_SCRATCH_BYTES of scratch";
     default: return status > 0 ? "HIP launch error (value is a hipError_t)" : "unknown status";
   }
 }

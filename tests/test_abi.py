@@ -233,3 +233,20 @@ def test_mfma_probe_validates():
     assert lib.moe_a8w4_mfma_probe(-1, 0, p, p, p, p, p, None) == abi.MOE_ERR_DIMS
     assert lib.moe_a8w4_mfma_probe(1, 0, p, None, p, p, p, None) == abi.MOE_ERR_NULL
     assert lib.moe_a8w4_mfma_probe(1, 0, ctypes.c_void_p((1 << 20) + 8), p, p, p, p, None) == abi.MOE_ERR_ALIGN
+
+
+def test_noalloc_entry_point_validates_before_touching_the_gpu():
+    """Oversized calls give MOE_ERR_SCRATCH, bad pointers their status, M = 0
+    succeeds; all before any HIP call (no GPU here)."""
+    lib = abi.load()
+    p = ctypes.c_void_p(1 << 20)
+    big = dims(tokens=16384, num_experts=385, topk=7)
+    assert abi.moe_a8w4_workspace_bytes(big) > abi.NOALLOC_SCRATCH_BYTES
+    assert lib.moe_a8w4_forward_noalloc(ctypes.byref(big), *([p] * 8), None) == abi.MOE_ERR_SCRATCH
+    d = dims(tokens=768, num_experts=384, topk=6)
+    assert abi.moe_a8w4_workspace_bytes(d) <= abi.NOALLOC_SCRATCH_BYTES
+    assert lib.moe_a8w4_forward_noalloc(ctypes.byref(d), *([p] * 7), None, None) == abi.MOE_ERR_NULL
+    assert lib.moe_a8w4_forward_noalloc(ctypes.byref(d), ctypes.c_void_p((1 << 20) + 4), *([p] * 7),
+                                        None) == abi.MOE_ERR_ALIGN
+    assert lib.moe_a8w4_forward_noalloc(ctypes.byref(dims(tokens=0)), *([None] * 8), None) == abi.MOE_OK
+    assert "scratch" in abi.status_str(abi.MOE_ERR_SCRATCH)
