@@ -17,7 +17,11 @@ experts' weights from HBM rather than from the 256 MB last-level cache.
 Printed: one JSON line with the mean microseconds per call over the sweep,
 per-bucket microseconds / GB/s / TFLOP/s, the roofline position of the
 dominant kernel (stage one, timed with HIP events on its stream inside the
-timed loop), and the CPU oracle timed on a bounded sample as a baseline.
+timed loop), the CPU oracle timed on every bucket as a baseline, and -- the
+MFMA-bound half of the metric -- a prefill block: the prefill geometry with
+the fused shared expert (385 experts, top-7) at 4096 and 16384 tokens and the
+local-slice geometry (96 of 384 experts, I 2304) at 16384 tokens, each call
+after a cache-evicting write, with the stage-one tile kernel's roofline.
 """
 from __future__ import annotations
 
@@ -52,6 +56,10 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="target CPU time of the oracle baseline sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-prefill", action="store_true",
+                    help="leave out the prefill block (the MFMA-bound half of the metric)")
+    ap.add_argument("--prefill-reps", type=int, default=10,
+                    help="timed calls per prefill point (median reported)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run a 1 GiB device copy (reference for HBM byte counters)")
     ap.add_argument("--profile-call", metavar="WORKLOAD:M", default=None,
@@ -109,7 +117,9 @@ def profile_call(args):
 
 def local_slice_table(args):
     """Median microseconds per moe_a8w4_forward call of the local-slice workload at
-    each token count of the pages' table, with algorithmic GB/s and TFLOP/s."""
+    each token count of the pages' table, with algorithmic GB/s and TFLOP/s.
+    Each timed call follows an untimed 1 GiB write, so even the 1-token call
+    (one or two experts, 12.5 MB each) streams its weights from HBM."""
     import torch
     from mixture_experts_fp8_amd import abi, workloads as wl
     dev = torch.device("cuda:0")
@@ -119,6 +129,7 @@ def local_slice_table(args):
     raw = [torch.from_numpy(np.ascontiguousarray(x)).to(dev) for x in host_w]
     packed = abi.moe_a8w4_pack_weights(d1, *raw)
     del raw, host_w
+    flush = torch.empty(FLUSH_BYTES, dtype=torch.uint8, device=dev)
     rows = {}
     for M in sorted(PAGES_LOCAL_SLICE_US):
         hidden, ids, wts = wl.make_inputs(w, M, "softmax")
@@ -134,6 +145,7 @@ def local_slice_table(args):
         ts = []
         for _ in range(max(3, args.steps)):
             e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            flush.zero_()   # evicts L2 and the last-level cache: the weights stream from HBM
             torch.cuda._sleep(HOST_COVER_CYCLES)   # the GPU waits while the host enqueues the call
             e0.record()
             abi.moe_a8w4_forward(d, x, idd, wd, *packed, out=out, workspace=ws)
@@ -336,11 +348,126 @@ def router_table(args):
                       "rows": rows}))
 
 
-def measured_traffic():
-    """Stage-one HBM bytes per launch from the committed counter summary, or None
-    if the kernel sources changed since those counters were taken."""
+# Prefill points of the metric's MFMA-bound half: the prefill geometry with the
+# fused shared expert (385 experts, top-7, I 640) at both token counts and both
+# routings' extreme (round-robin spreads every expert evenly), and the
+# local-slice geometry at its largest token count of the pages' table.
+PREFILL_POINTS = (("prefill-shared", 4096, "roundrobin"), ("prefill-shared", 16384, "roundrobin"),
+                  ("prefill-shared", 16384, "softmax"), ("local-slice", 16384, "softmax"))
+FLUSH_BYTES = 1 << 30   # written before every timed prefill call: evicts L2 and the 256 MB last-level cache
+
+
+def prefill_block(args, lib, stream):
+    """Median microseconds per call at each prefill point, step by step with
+    HIP events on the launch stream (the launch sequence of moe_a8w4_forward),
+    each call preceded by an untimed 1 GiB write so that the weights stream
+    from HBM; returns (rows, roofline of the stage-one tile kernel at the
+    prefill geometry's 16384-token round-robin point)."""
+    import torch
+    from mixture_experts_fp8_amd import abi, workloads as wl
+    dev = torch.device("cuda:0")
+    sp = ctypes.c_void_p(stream.cuda_stream)
+    vp = lambda t: ctypes.c_void_p(t.data_ptr())
+    flush = torch.empty(FLUSH_BYTES, dtype=torch.uint8, device=dev)
+    rows, roof = {}, None
+    for name in dict.fromkeys(p[0] for p in PREFILL_POINTS):
+        w = wl.WORKLOADS[name]
+        t0 = time.time()
+        host_w = wl.make_weights(w)
+        d1 = abi.make_dims(1, w.hidden, w.inter, w.num_experts, w.topk, w.expert_offset)
+        raw = [torch.from_numpy(np.ascontiguousarray(x)).to(dev) for x in host_w]
+        packed = abi.moe_a8w4_pack_weights(d1, *raw)
+        del raw, host_w
+        torch.cuda.synchronize()
+        print("prefill setup %s: %.1f s" % (name, time.time() - t0), file=sys.stderr, flush=True)
+        for _, M, mode in (p for p in PREFILL_POINTS if p[0] == name):
+            hidden, ids, wts = wl.make_inputs(w, M, mode)
+            d = abi.make_dims(M, w.hidden, w.inter, w.num_experts, w.topk, w.expert_offset, w.routed_experts)
+            bm = abi.moe_a8w4_block_m(d)
+            cap = abi.moe_a8w4_sort_capacity(d, bm)
+            x = torch.from_numpy(hidden.view(np.int16)).to(dev).view(torch.bfloat16)
+            idd, wd = torch.from_numpy(ids).to(dev), torch.from_numpy(wts).to(dev)
+            aq = torch.empty((M, w.hidden), dtype=torch.uint8, device=dev)
+            as_ = torch.empty((M, w.hidden // 32), dtype=torch.uint8, device=dev)
+            srt = torch.empty(cap, dtype=torch.int32, device=dev)
+            bexp = torch.empty(cap // bm, dtype=torch.int32, device=dev)
+            npad = torch.empty(1, dtype=torch.int32, device=dev)
+            iq = torch.empty((cap, w.inter), dtype=torch.uint8, device=dev)
+            is_ = torch.empty((cap, w.inter // 32), dtype=torch.uint8, device=dev)
+            y = torch.empty(abi.route_rows_bytes(d), dtype=torch.uint8, device=dev)
+            out = torch.empty((M, w.hidden), dtype=torch.bfloat16, device=dev)
+            dref = ctypes.byref(d)
+            steps = (
+                (lib.moe_a8w4_quant_sort, (dref, ctypes.c_int32(bm), vp(x), vp(idd), vp(aq), vp(as_), vp(srt),
+                                           vp(bexp), vp(npad), sp)),
+                (lib.moe_a8w4_stage1, (dref, ctypes.c_int32(bm), vp(aq), vp(as_), vp(srt), vp(bexp), vp(npad),
+                                       vp(packed[0]), vp(packed[1]), vp(iq), vp(is_), sp)),
+                (lib.moe_a8w4_stage2, (dref, ctypes.c_int32(bm), vp(iq), vp(is_), vp(srt), vp(bexp), vp(npad),
+                                       vp(wd), vp(packed[2]), vp(packed[3]), vp(y), sp)),
+                (lib.moe_a8w4_combine, (dref, vp(idd), vp(y), vp(out), sp)),
+            )
+
+            def call(ev=None):
+                for i, (fn, a) in enumerate(steps):
+                    if ev is not None:
+                        ev[i].record(stream)
+                    if fn(*a):
+                        raise RuntimeError("prefill step %d failed" % i)
+                if ev is not None:
+                    ev[len(steps)].record(stream)
+
+            for _ in range(2):
+                call()
+            torch.cuda.synchronize()
+            t = []
+            for _ in range(max(3, args.prefill_reps)):
+                ev = [torch.cuda.Event(enable_timing=True) for _ in range(len(steps) + 1)]
+                flush.zero_()
+                torch.cuda._sleep(HOST_COVER_CYCLES)
+                call(ev)
+                ev[-1].synchronize()
+                t.append([ev[i].elapsed_time(ev[i + 1]) * 1e3 for i in range(len(steps))])
+            t = np.array(t)
+            per_call = t.sum(axis=1)
+            us = float(np.median(per_call))
+            a = algorithmic(w, M, ids)
+            tf = a["flops"] / us / 1e6
+            st1 = float(np.median(t[:, 1]))
+            row = dict(us_per_call=round(us, 1), us_p10=round(float(np.percentile(per_call, 10)), 1),
+                       us_p90=round(float(np.percentile(per_call, 90)), 1), routes=a["R"], block_m=bm,
+                       TFLOPs=round(tf, 1), mfma_frac_fp8_rate=round(tf / FP8_PEAK_TFLOPS, 4),
+                       mfma_frac_fp4_peak=round(tf / FP4_PEAK_TFLOPS, 4),
+                       step_us=dict(zip(("prep", "stage1", "stage2", "combine"),
+                                        [round(float(v), 1) for v in np.median(t, axis=0)])),
+                       stage1_TFLOPs=round(a["stage1_flops"] / st1 / 1e6, 1))
+            key = "%s:%d:%s" % (name, M, mode)
+            rows[key] = row
+            print("prefill %s  %s" % (key, row), file=sys.stderr, flush=True)
+            if (name, M, mode) == ("prefill-shared", 16384, "roundrobin"):
+                ach = a["stage1_flops"] / float(np.mean(t[:, 1])) / 1e6
+                roof = dict(bound="mfma", achieved=round(ach, 1), peak=FP8_PEAK_TFLOPS, unit="TFLOP/s",
+                            frac=round(ach / FP8_PEAK_TFLOPS, 4), traffic=measured_traffic("prefill"),
+                            frac_of_fp4_peak=round(ach / FP4_PEAK_TFLOPS, 4),
+                            kernel="stage-one tile kernel (tile_kernel<1,4,3,false,true>)",
+                            workload=key, flops_per_launch=a["stage1_flops"],
+                            launch_us_mean=round(float(np.mean(t[:, 1])), 1),
+                            peak_note="the A operand is FP8, so the instruction issues at the FP8 rate "
+                                      "(5.0 PFLOP/s); frac_of_fp4_peak is against 10.1")
+            del x, idd, wd, aq, as_, srt, bexp, npad, iq, is_, y, out
+        del packed
+        torch.cuda.empty_cache()
+    del flush
+    torch.cuda.empty_cache()
+    return rows, roof
+
+
+def measured_traffic(which="decode"):
+    """Stage-one HBM bytes per launch from the committed counter summary (the
+    decode sweep, or the prefill geometry's 16384-token call), or None if the
+    kernel sources changed since those counters were taken."""
     import hashlib
-    path = os.path.join(ROOT, "profiles", "hbm_traffic_backbone_decode_sweep.md")
+    path = os.path.join(ROOT, "profiles", {"decode": "hbm_traffic_backbone_decode_sweep.md",
+                                           "prefill": "hbm_traffic_prefill_shared_16384.md"}[which])
     if not os.path.exists(path):
         return None
     for line in open(path):
@@ -522,6 +649,11 @@ def main():
                     bytes_per_launch_mean=round(s1_bytes / len(buckets)),
                     launch_us_mean=round(s1_time / len(buckets), 2))
 
+    prefill = roof_prefill = None
+    if not args.no_prefill:
+        # the prefill geometries add about 2 GB of weights each (HBM holds 288 GB)
+        prefill, roof_prefill = prefill_block(args, lib, stream)
+
     value = ms_per_step * 1e3 / len(buckets)
     result = {
         "metric": METRIC, "value": round(value, 2), "unit": "us/call", "n_gpus": 1,
@@ -533,29 +665,39 @@ def main():
                    "tokens": list(BUCKETS), "value": "mean us per call over the eight buckets"},
         "buckets": per_bucket, "roofline": roofline,
     }
+    if prefill is not None:
+        result["prefill"] = dict(
+            unit="us/call", note="MFMA-bound half of the metric: median of %d calls, each after an untimed "
+                                 "1 GiB write (weights stream from HBM); step_us from HIP events around each "
+                                 "launch; fractions of the dense MFMA peaks (FP8 rate 5.0, FP4 10.1 PFLOP/s)"
+                                 % max(3, args.prefill_reps),
+            points=prefill)
+        result["roofline_prefill"] = roof_prefill
 
-    # ---- CPU baseline: the oracle on a bounded sample of the same workload
+    # ---- CPU baseline: the oracle, one whole call per decode bucket (every
+    # token), median of up to three calls while a bucket takes under 10 s
     if not args.no_cpu_baseline:
         import oracle
-        b = buckets[-1]
-        hidden = b["x"].view(torch.int16).cpu().numpy().view(np.uint16)
-        wts = b["wd"].cpu().numpy()
-        rng = np.random.default_rng(0)
-        n = 4
-        t = time.perf_counter()
-        oracle.forward(hidden, b["ids"], wts, *host_w, tokens=rng.choice(b["M"], n, replace=False))
-        dt = time.perf_counter() - t
-        n2 = int(max(n, n * args.cpu_seconds / max(dt, 1e-3)))
-        tok = rng.choice(b["M"], n2, replace=True)   # tokens may repeat: each is computed afresh
-        t = time.perf_counter()
-        oracle.forward(hidden, b["ids"], wts, *host_w, tokens=tok)
-        dt = time.perf_counter() - t
-        per_route = dt / (n2 * w.topk)
-        mean_us = float(np.mean([bb["alg"]["R"] * per_route * 1e6 for bb in buckets]))
+        per = {}
+        t_all = time.perf_counter()
+        for b in buckets:
+            hidden = b["x"].view(torch.int16).cpu().numpy().view(np.uint16)
+            wts = b["wd"].cpu().numpy()
+            ts = []
+            for _ in range(3):
+                t = time.perf_counter()
+                oracle.forward(hidden, b["ids"], wts, *host_w)
+                ts.append(time.perf_counter() - t)
+                if ts[-1] > 10.0:
+                    break
+            per[str(b["M"])] = round(float(np.median(ts)) * 1e6, 1)
+            print("oracle M=%d: %.3f s per call" % (b["M"], np.median(ts)), file=sys.stderr, flush=True)
+        mean_us = float(np.mean(list(per.values())))
         result["cpu_baseline"] = dict(
             value=round(mean_us, 1), unit="us/call", cores=oracle.num_threads(), kind="oracle",
-            sample="%d tokens (%d routes) of the M=768 bucket in %.1f s, scaled by each bucket's "
-                   "routes; mean over the eight buckets" % (n2, n2 * w.topk, dt))
+            sample="every token of each of the eight buckets, median of up to 3 calls per bucket "
+                   "(%.1f s in all); mean over the buckets" % (time.perf_counter() - t_all),
+            per_bucket_us=per)
     if args.calibrate_copy:
         # a plain copy of known size: 1 GiB read + 1 GiB written per launch
         src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
