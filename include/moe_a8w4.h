@@ -79,16 +79,22 @@ typedef struct moe_a8w4_dims {
 /* ------------------------------------------------------------------ sizes */
 
 /* Bytes of workspace moe_a8w4_forward needs for these dims (an upper bound
- * independent of the routing).  Writes *bytes; returns a status. */
+ * independent of the routing): the values one call passes between its steps
+ * -- quantised activations, the sort, the re-quantised intermediate, the
+ * weighted route rows (aiter PR 5904, "Fused-MoE kernel, expert-parallel
+ * benchmark": one call spans sorting, both GEMMs and the re-quantisation
+ * between them).  Writes *bytes; returns a status. */
 int moe_a8w4_workspace_bytes(const moe_a8w4_dims* dims, size_t* bytes);
 
 /* Rows per sorted block (16, 32, 64 or 128) that moe_a8w4_forward uses for
  * these dims: a function of the mean routes per expert,
  * M * topk / max(num_experts, routed_experts), only.  Negative status if
- * invalid.  The same block_m is shared by the sort and both stages. */
+ * invalid.  The same block_m is shared by the sort and both stages (aiter
+ * PR 5609, Commands run: the sort's block must equal the stage-two tile). */
 int moe_a8w4_block_m(const moe_a8w4_dims* dims);
 
-/* Capacity, in entries, that sorted_ids needs for these dims and block_m:
+/* Capacity, in entries, that sorted_ids needs for these dims and block_m
+ * (every expert's run padded to a multiple of block_m, as the sort emits it):
  * R + min(E, R) * (block_m - 1) rounded up to block_m, R = M * topk.
  * block_expert needs capacity / block_m entries.  Negative status if invalid. */
 int64_t moe_a8w4_sort_capacity(const moe_a8w4_dims* dims, int32_t block_m);
@@ -96,8 +102,15 @@ int64_t moe_a8w4_sort_capacity(const moe_a8w4_dims* dims, int32_t block_m);
 /* ---------------------------------------------------------------- weights */
 
 /* Reorder MXFP4 expert weights into the layout the GEMM kernels stream
- * (a one-time, off-path transform; the packed buffers have the same sizes as
- * the inputs).  Inputs, row-major, element 2i in the low nibble of byte i:
+ * (a one-time, off-path transform, part of this interface: moe_a8w4_forward
+ * and the step entry points take its outputs; the packed buffers have the
+ * same sizes as the inputs).  The weights are those of aiter PR 5609,
+ * "Add DeepSeek V4.1 Flash TP4 gfx950 MoE tuning", Configuration (MXFP4 with
+ * one E8M0 scale per 32 along K, gate and up rows interleaved).  Packing is a
+ * permutation of bytes, so the layer computes exactly what it would on the
+ * raw layout; reading the raw layout in the order the matrix instruction
+ * wants instead streams at 2.4 TB/s against 6.7 TB/s (measured, decode stage
+ * one).  Inputs, row-major, element 2i in the low nibble of byte i:
  *   w13      [E, 2I, H/2]  E2M1 codes; row 2j = gate of column j, row 2j+1 = up
  *   w13_s    [E, 2I, H/32] E8M0 scale of each run of 32 elements along H
  *   w2       [E, H, I/2]   E2M1 codes
@@ -170,18 +183,24 @@ int moe_a8w4_forward_routed(const moe_a8w4_dims* dims, const void* hidden, const
 
 /* ----------------------------------------------- the steps, one at a time */
 
-/* Per-1x32 FP8 quantisation of BF16 rows: x [M, H] -> q [M, H] E4M3 codes,
- * s [M, H/32] E8M0 codes.  H must be a multiple of 32. */
+/* Per-1x32 FP8 quantisation of BF16 rows (the activation quantisation of
+ * aiter PR 5609, Configuration: FP8 activations, per-1x32 scaling; OCP MX
+ * v1.0 conversion): x [M, H] -> q [M, H] E4M3 codes, s [M, H/32] E8M0 codes.
+ * H must be a multiple of 32; every pointer 16-byte aligned. */
 int moe_a8w4_quant_act(int32_t M, int32_t H, const void* x, uint8_t* q, uint8_t* s,
                        hipStream_t stream);
 
-/* Group local routes by expert: sorted_ids [capacity] receives, expert by
+/* The sorting step of one call (aiter PR 5904, "Fused-MoE kernel,
+ * expert-parallel benchmark": sorting is part of the timed call; aiter PR
+ * 5609, Commands run: its block size matches the stage-two tile).
+ * Group local routes by expert: sorted_ids [capacity] receives, expert by
  * expert in ascending local id, the expert's routes in ascending t*topk + k
  * as (k << 24) | t, each expert's run padded with M to a multiple of block_m
  * (experts without routes get no rows); block_expert [capacity/block_m]
  * receives the local expert of each block; num_padded [1] the total rows.
- * Entries past num_padded are left unspecified.  One workgroup sorts;
- * the result does not depend on timing (bitwise repeatable). */
+ * Entries past num_padded are left unspecified.  The result does not
+ * depend on timing (bitwise repeatable).  Every pointer 16-byte aligned
+ * (topk_ids is read 16 bytes at a time), else MOE_ERR_ALIGN. */
 int moe_a8w4_sort(const moe_a8w4_dims* dims, int32_t block_m, const int32_t* topk_ids,
                   int32_t* sorted_ids, int32_t* block_expert, int32_t* num_padded,
                   hipStream_t stream);
@@ -193,7 +212,10 @@ int moe_a8w4_quant_sort(const moe_a8w4_dims* dims, int32_t block_m, const void* 
                         const int32_t* topk_ids, uint8_t* a_q, uint8_t* a_s, int32_t* sorted_ids,
                         int32_t* block_expert, int32_t* num_padded, hipStream_t stream);
 
-/* Stage one for every sorted block: inter_q [capacity, I] E4M3 codes and
+/* Stage one of aiter PR 5609, Configuration (gate/up GEMM on interleaved
+ * rows, SiLU(gate) * up, no routing weight) with the intermediate
+ * quantisation of aiter PR 5904, "Fused-MoE kernel, expert-parallel
+ * benchmark", for every sorted block: inter_q [capacity, I] E4M3 codes and
  * inter_s [capacity, I/32] E8M0 codes, row p = sorted position, holding the
  * per-1x32 quantisation of SiLU(gate) * up.  Rows of blocks that hold a
  * route are written in full (padding columns included); rows past the last
@@ -203,7 +225,9 @@ int moe_a8w4_stage1(const moe_a8w4_dims* dims, int32_t block_m, const uint8_t* a
                     const int32_t* num_padded, const uint8_t* w13_p, const uint8_t* w13_s_p,
                     uint8_t* inter_q, uint8_t* inter_s, hipStream_t stream);
 
-/* Stage two: for every local route (t, k), row (t, k) of y_routes receives
+/* Stage two of aiter PR 5609, Configuration (down projection; the routing
+ * weight applied here, not in stage one): for every local route (t, k), row
+ * (t, k) of y_routes receives
  * topk_weights[t,k] * (w2[e] h), h its dequantised intermediate, in the
  * route-row format: y_routes holds [M, topk, H] int16 codes followed by
  * [M, topk, H/32] uint8 exponents, M*topk*(2H + H/32) bytes in all (16-byte
@@ -218,7 +242,8 @@ int moe_a8w4_stage2(const moe_a8w4_dims* dims, int32_t block_m, const uint8_t* i
                     const int32_t* num_padded, const float* topk_weights, const uint8_t* w2_p,
                     const uint8_t* w2_s_p, void* y_routes, hipStream_t stream);
 
-/* Top-k combine: out[t, :] (BF16, [M, H]) = round-to-nearest-even of the
+/* Top-k combine into the BF16 output of aiter PR 5609, Configuration:
+ * out[t, :] (BF16, [M, H]) = round-to-nearest-even of the
  * float32 sum, in ascending k, of the decoded rows (t, k, :) of y_routes (the
  * stage-two route rows) over the token's local slots (topk_ids decides which
  * slots are local); zero for a token without one.  Bitwise repeatable. */
