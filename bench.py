@@ -416,11 +416,27 @@ def prefill_block(args, lib, stream):
                 if ev is not None:
                     ev[len(steps)].record(stream)
 
+            ws = torch.empty(abi.moe_a8w4_workspace_bytes(d), dtype=torch.uint8, device=dev)
+            a_fwd = (dref, vp(x), vp(idd), vp(wd), vp(packed[0]), vp(packed[1]), vp(packed[2]), vp(packed[3]),
+                     vp(out), vp(ws), ctypes.c_size_t(ws.numel()), sp)
             for _ in range(2):
                 call()
+                lib.moe_a8w4_forward(*a_fwd)
             torch.cuda.synchronize()
-            t = []
+            t, per_call = [], []
             for _ in range(max(3, args.prefill_reps)):
+                # the call as the library runs it (moe_a8w4_forward) ...
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                flush.zero_()
+                torch.cuda._sleep(HOST_COVER_CYCLES)
+                e0.record(stream)
+                if lib.moe_a8w4_forward(*a_fwd):
+                    raise RuntimeError("moe_a8w4_forward failed")
+                e1.record(stream)
+                e1.synchronize()
+                per_call.append(e0.elapsed_time(e1) * 1e3)
+                # ... and step by step through the step entry points (the
+                # combine as a launch of its own), for the per-step times
                 ev = [torch.cuda.Event(enable_timing=True) for _ in range(len(steps) + 1)]
                 flush.zero_()
                 torch.cuda._sleep(HOST_COVER_CYCLES)
@@ -428,7 +444,7 @@ def prefill_block(args, lib, stream):
                 ev[-1].synchronize()
                 t.append([ev[i].elapsed_time(ev[i + 1]) * 1e3 for i in range(len(steps))])
             t = np.array(t)
-            per_call = t.sum(axis=1)
+            per_call = np.array(per_call)
             us = float(np.median(per_call))
             a = algorithmic(w, M, ids)
             tf = a["flops"] / us / 1e6
@@ -439,6 +455,7 @@ def prefill_block(args, lib, stream):
                        mfma_frac_fp4_peak=round(tf / FP4_PEAK_TFLOPS, 4),
                        step_us=dict(zip(("prep", "stage1", "stage2", "combine"),
                                         [round(float(v), 1) for v in np.median(t, axis=0)])),
+                       steps_sum_us=round(float(np.median(t.sum(axis=1))), 1),
                        stage1_TFLOPs=round(a["stage1_flops"] / st1 / 1e6, 1))
             key = "%s:%d:%s" % (name, M, mode)
             rows[key] = row
@@ -453,7 +470,7 @@ def prefill_block(args, lib, stream):
                             launch_us_mean=round(float(np.mean(t[:, 1])), 1),
                             peak_note="the A operand is FP8, so the instruction issues at the FP8 rate "
                                       "(5.0 PFLOP/s); frac_of_fp4_peak is against 10.1")
-            del x, idd, wd, aq, as_, srt, bexp, npad, iq, is_, y, out
+            del x, idd, wd, aq, as_, srt, bexp, npad, iq, is_, y, out, ws
         del packed
         torch.cuda.empty_cache()
     del flush
@@ -667,9 +684,11 @@ def main():
     }
     if prefill is not None:
         result["prefill"] = dict(
-            unit="us/call", note="MFMA-bound half of the metric: median of %d calls, each after an untimed "
-                                 "1 GiB write (weights stream from HBM); step_us from HIP events around each "
-                                 "launch; fractions of the dense MFMA peaks (FP8 rate 5.0, FP4 10.1 PFLOP/s)"
+            unit="us/call", note="MFMA-bound half of the metric: median of %d moe_a8w4_forward calls, each "
+                                 "after an untimed 1 GiB write (weights stream from HBM); step_us from HIP events "
+                                 "around each launch of the same call made through the step entry points, where "
+                                 "the top-k combine is a launch of its own (the call folds it into stage two); "
+                                 "fractions of the dense MFMA peaks (FP8 rate 5.0, FP4 10.1 PFLOP/s)"
                                  % max(3, args.prefill_reps),
             points=prefill)
         result["roofline_prefill"] = roof_prefill

@@ -173,13 +173,17 @@ def test_edge_cases():
     assert abi.load().moe_a8w4_forward(d0, *([None] * 9), 0, None) == abi.MOE_OK
 
 
-def test_steps_compose_to_forward():
-    w = wl.scaled(wl.WORKLOADS["draft-sweep"], num_experts=16, routed_experts=16, config_id=121)
+@pytest.mark.parametrize("E,M,want_bm", [(16, 80, 32), (16, 200, 64), (8, 400, 128)])
+def test_steps_compose_to_forward(E, M, want_bm):
+    """The step entry points (stage two writing route rows, then the separate
+    combine) give the forward's output bit for bit, whether the forward runs
+    the separate combine (blocks of 16/32) or folds it into stage two (64/128)."""
+    w = wl.scaled(wl.WORKLOADS["draft-sweep"], num_experts=E, routed_experts=E, config_id=121)
     layer = Layer(w)
-    M = 80
     hidden, ids, wts = wl.make_inputs(w, M, "softmax")
     d = layer.dims(M)
     bm = abi.moe_a8w4_block_m(d)
+    assert bm == want_bm
     note("steps M=%d bm=%d" % (M, bm))
     xd, idd, wd = dev(hidden), dev(ids), dev(wts)
     q, s = abi.moe_a8w4_quant_act(xd)
