@@ -355,6 +355,153 @@ __global__ void __launch_bounds__(256) fused_kernel(GemmArgs a1, GemmArgs a2, Fu
   }
 }
 
+// Stage two for a short reduction (K = I = 128 KS, KS <= 5) at decode block
+// sizes (16 NCG routes): the tile of run_tile with one wave per 64-row group
+// (4 row groups, 256 output columns per workgroup, every K step), except
+// that (1) the block's intermediate rows, the B operand all four waves
+// share, are loaded once per workgroup into LDS (piece p of token t's 128-byte
+// step row in slot p ^ ((t >> 1) & 7), so the 16 lanes of one operand read
+// hit distinct bank slots) instead of once per wave, and (2) each wave issues
+// the weight fragments of all KS steps before its first MFMA: KS x 4 KB in
+// flight per wave, one memory latency per tile instead of one per prefetch
+// window.  Same MFMA sequence per output, so the same result bit for bit.
+template <int NCG, int KS>
+__global__ void __launch_bounds__(256) short_k_kernel(GemmArgs args) {
+  constexpr int BM = 16 * NCG;
+  constexpr int PIECES = KS * BM * 8;            // 16-byte pieces of the block's B rows
+  __shared__ __attribute__((aligned(16))) uint8_t sB[PIECES * 16];   // [step][token][slot]
+  __shared__ __attribute__((aligned(16))) uint32_t sBs[BM * KS];      // token scales [token][step]
+  __shared__ __attribute__((aligned(16))) uint8_t scr_all[4][kStage2Scratch];
+  const int N = args.N, M = args.M;
+  constexpr int K = KS * 128;
+  const int NG = N / 256;
+  const int nblk = *args.num_padded / BM;
+  const int T = nblk * NG;
+  if ((int)blockIdx.x >= T) return;
+  const int tile = xcd_tile(blockIdx.x, T);
+  const int b = tile / NG, wgg = tile - b * NG;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int grp = wgg * 4 + wave;
+  const int t16 = lane & 15, g = lane >> 4;
+  const int32_t* ids = args.sorted_ids + (int64_t)b * BM;
+
+  int rid[NCG];
+  int nact = 0;
+#pragma unroll
+  for (int c = 0; c < NCG; ++c) {
+    rid[c] = ids[c * 16 + t16];
+    if (__ballot(rid[c] != M) != 0) nact = c + 1;
+  }
+  const int e = args.block_expert[b];
+
+  // B rows of the block (sorted positions b BM .. + BM, contiguous in the
+  // intermediate) and their scale words, into registers first
+  constexpr int PER_THREAD = (PIECES + 255) / 256;
+  v4i piece[PER_THREAD];
+  const uint8_t* brows = args.bq + (int64_t)b * BM * K;
+#pragma unroll
+  for (int i = 0; i < PER_THREAD; ++i) {
+    const int q = (int)threadIdx.x + 256 * i;     // LDS piece q = (s BM + t) 8 + slot
+    if (q < PIECES) {
+      const int slot = q & 7, t = (q >> 3) % BM, st = (q >> 3) / BM;
+      const int p = slot ^ ((t >> 1) & 7);
+      piece[i] = *reinterpret_cast<const v4i*>(brows + (int64_t)t * K + st * 128 + p * 16);
+    }
+  }
+  uint32_t sword = 0;
+  if ((int)threadIdx.x < BM * KS) {
+    const int t = threadIdx.x / KS, st = threadIdx.x - t * KS;
+    sword = *reinterpret_cast<const uint32_t*>(args.bs + ((int64_t)b * BM + t) * (K / 32) + 4 * st);
+  }
+
+  // every K step's weight fragments of this wave's 64 rows
+  const uint8_t* wp = args.w + (int64_t)e * ((int64_t)N * K / 2) + (int64_t)grp * KS * 4096 + lane * 16;
+  const uint8_t* wsp = args.ws + (int64_t)e * ((int64_t)N * K / 32) + (int64_t)grp * KS * 256 + lane * 4;
+  v4i a[KS][4];
+  uint32_t sa[KS];
+#pragma unroll
+  for (int st = 0; st < KS; ++st) {
+#pragma unroll
+    for (int t = 0; t < 4; ++t) a[st][t] = __builtin_nontemporal_load(reinterpret_cast<const v4i*>(wp + st * 4096 + t * 1024));
+    sa[st] = __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(wsp + st * 256));
+  }
+
+  // the routes' slots and routing weights, for the epilogue
+  int64_t slot[NCG];
+  float wt[NCG];
+#pragma unroll
+  for (int c = 0; c < NCG; ++c) {
+    const bool v = rid[c] != M;
+    slot[c] = v ? route_slot(rid[c], args.topk) : -1;
+    wt[c] = v ? args.topk_weights[slot[c]] : 0.f;
+  }
+
+#pragma unroll
+  for (int i = 0; i < PER_THREAD; ++i) {
+    const int q = (int)threadIdx.x + 256 * i;
+    if (q < PIECES) *reinterpret_cast<v4i*>(sB + q * 16) = piece[i];
+  }
+  if ((int)threadIdx.x < BM * KS) sBs[threadIdx.x] = sword;
+  // the LDS writes of every wave are done (the barrier alone does not wait
+  // for the weight loads still in flight)
+  __builtin_amdgcn_s_waitcnt(15 | (3 << 14) | (7 << 4));   // lgkmcnt(0) only
+  __asm__ volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  __asm__ volatile("" ::: "memory");
+
+  v4f acc[4][NCG];
+#pragma unroll
+  for (int t = 0; t < 4; ++t)
+#pragma unroll
+    for (int c = 0; c < NCG; ++c) acc[t][c] = v4f{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int st = 0; st < KS; ++st) {
+#pragma unroll
+    for (int c = 0; c < NCG; ++c) {
+      if (c < nact) {
+        const int tok = c * 16 + t16;
+        const int sw = (tok >> 1) & 7;
+        const uint8_t* row = sB + (st * BM + tok) * 128;
+        const v8i bb = join8(*reinterpret_cast<const v4i*>(row + ((g ^ sw) << 4)),
+                             *reinterpret_cast<const v4i*>(row + (((4 + g) ^ sw) << 4)));
+        const uint32_t sb = (sBs[tok * KS + st] >> (8 * g)) & 0xFFu;
+        acc[0][c] = mfma_fp4_fp8<0>(a[st][0], bb, acc[0][c], sa[st], sb);
+        acc[1][c] = mfma_fp4_fp8<1>(a[st][1], bb, acc[1][c], sa[st], sb);
+        acc[2][c] = mfma_fp4_fp8<2>(a[st][2], bb, acc[2][c], sa[st], sb);
+        acc[3][c] = mfma_fp4_fp8<3>(a[st][3], bb, acc[3][c], sa[st], sb);
+      }
+    }
+  }
+
+  uint8_t* scr = &scr_all[wave][0];
+#pragma unroll
+  for (int c = 0; c < NCG; ++c) {
+    if (c < nact) {
+      const v4f part[4] = {acc[0][c], acc[1][c], acc[2][c], acc[3][c]};
+      stage2_store(part, slot[c], wt[c], args, grp, g, scr);
+    }
+  }
+}
+
+template <int NCG, int KS>
+hipError_t launch_short_k(const GemmArgs& a, int64_t max_blocks, hipStream_t stream) {
+  const int64_t grid = max_blocks * (a.N / 256);
+  if (grid <= 0) return hipSuccess;
+  hipLaunchKernelGGL((short_k_kernel<NCG, KS>), dim3((unsigned)grid), dim3(256), 0, stream, a);
+  return hipGetLastError();
+}
+
+template <int NCG>
+hipError_t launch_stage2_short(const GemmArgs& a, int64_t max_blocks, hipStream_t stream) {
+  switch (a.K / 128) {
+    case 1: return launch_short_k<NCG, 1>(a, max_blocks, stream);
+    case 2: return launch_short_k<NCG, 2>(a, max_blocks, stream);
+    case 3: return launch_short_k<NCG, 3>(a, max_blocks, stream);
+    case 4: return launch_short_k<NCG, 4>(a, max_blocks, stream);
+    default: return launch_short_k<NCG, 5>(a, max_blocks, stream);
+  }
+}
+
 template <int STAGE, int NCG, int NWK, int PD, bool NT>
 hipError_t launch_gemm(const GemmArgs& a, int64_t max_blocks, hipStream_t stream) {
   constexpr int NWR = 4 / NWK;
@@ -412,11 +559,15 @@ hipError_t launch_stage1(const GemmArgs& a, int64_t max_blocks, hipStream_t stre
 // to hide that behind other workgroups (local slice, 1 token: 38 -> 31 us).
 // At I = 640 (5 steps), or with blocks of 32, a split measured no gain.
 hipError_t launch_stage2(const GemmArgs& a, int64_t max_blocks, hipStream_t stream) {
+  const bool short_k = a.K <= 640 && a.N % 256 == 0;   // K is a multiple of 128
   switch (a.bm) {
     case 16:
+      if (short_k) return launch_stage2_short<1>(a, max_blocks, stream);
       return a.K >= 1024 ? launch_gemm<2, 1, 4, MOE_S2_PD, MOE_NT_SMALL>(a, max_blocks, stream)
                          : launch_gemm<2, 1, 1, MOE_S2_PD, MOE_NT_SMALL>(a, max_blocks, stream);
-    case 32: return launch_gemm<2, 2, 1, MOE_S2_PD, MOE_NT_SMALL>(a, max_blocks, stream);
+    case 32:
+      if (short_k) return launch_stage2_short<2>(a, max_blocks, stream);
+      return launch_gemm<2, 2, 1, MOE_S2_PD, MOE_NT_SMALL>(a, max_blocks, stream);
     case 64:
     case 128: return launch_tile(2, a, max_blocks, stream);
     default: return hipErrorInvalidValue;
