@@ -65,6 +65,8 @@ def parse():
     ap.add_argument("--profile-call", metavar="WORKLOAD:M", default=None,
                     help="instead of the decode sweep: --steps calls of moe_a8w4_forward for one "
                          "workload and token count (a short run to put under a profiler)")
+    ap.add_argument("--back-to-back", action="store_true",
+                    help="with --profile-call: no 1 GiB write between the calls")
     ap.add_argument("--local-slice-table", action="store_true",
                     help="instead of the decode sweep: one call per token count of the local-slice "
                          "workload (the pages' own MI355X fused_moe timing table) as a JSON line")
@@ -109,10 +111,32 @@ def profile_call(args):
     wd = torch.from_numpy(wts).to(dev)
     out = torch.empty((M, w.hidden), dtype=torch.bfloat16, device=dev)
     ws = torch.empty(abi.moe_a8w4_workspace_bytes(d), dtype=torch.uint8, device=dev)
+    # each call after an untimed 1 GiB write, as the prefill block times it
+    # (--back-to-back: the calls one after another, with nothing between)
+    flush = None if args.back_to_back else torch.empty(FLUSH_BYTES, dtype=torch.uint8, device=dev)
     for _ in range(args.steps):
+        if flush is not None:
+            flush.zero_()
+            torch.cuda._sleep(HOST_COVER_CYCLES)
         abi.moe_a8w4_forward(d, x, idd, wd, *packed, out=out, workspace=ws)
     torch.cuda.synchronize()
-    print(json.dumps({"profile_call": args.profile_call, "calls": args.steps}))
+    rec = {"profile_call": args.profile_call, "calls": args.steps, "back_to_back": args.back_to_back}
+    if args.calibrate_copy:
+        del x, out, ws, flush
+        rec["calibration_copy_bytes"] = calibration_copy(dev)
+    print(json.dumps(rec))
+
+
+def calibration_copy(dev):
+    """Three device copies of 1 GiB (1 GiB read + 1 GiB written per launch):
+    the reference against which HBM byte counters are scaled."""
+    import torch
+    src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    return 1 << 30
 
 
 def local_slice_table(args):
@@ -443,6 +467,16 @@ def prefill_block(args, lib, stream):
                 call(ev)
                 ev[-1].synchronize()
                 t.append([ev[i].elapsed_time(ev[i + 1]) * 1e3 for i in range(len(steps))])
+            # sustained rate: the same calls one after another, nothing between
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            torch.cuda._sleep(HOST_COVER_CYCLES)
+            e0.record(stream)
+            for _ in range(max(3, args.prefill_reps)):
+                if lib.moe_a8w4_forward(*a_fwd):
+                    raise RuntimeError("moe_a8w4_forward failed")
+            e1.record(stream)
+            e1.synchronize()
+            b2b = e0.elapsed_time(e1) * 1e3 / max(3, args.prefill_reps)
             t = np.array(t)
             per_call = np.array(per_call)
             us = float(np.median(per_call))
@@ -450,7 +484,8 @@ def prefill_block(args, lib, stream):
             tf = a["flops"] / us / 1e6
             st1 = float(np.median(t[:, 1]))
             row = dict(us_per_call=round(us, 1), us_p10=round(float(np.percentile(per_call, 10)), 1),
-                       us_p90=round(float(np.percentile(per_call, 90)), 1), routes=a["R"], block_m=bm,
+                       us_p90=round(float(np.percentile(per_call, 90)), 1),
+                       us_per_call_back_to_back=round(b2b, 1), routes=a["R"], block_m=bm,
                        TFLOPs=round(tf, 1), mfma_frac_fp8_rate=round(tf / FP8_PEAK_TFLOPS, 4),
                        mfma_frac_fp4_peak=round(tf / FP4_PEAK_TFLOPS, 4),
                        step_us=dict(zip(("prep", "stage1", "stage2", "combine"),
@@ -686,10 +721,11 @@ def main():
         result["prefill"] = dict(
             unit="us/call", note="MFMA-bound half of the metric: median of %d moe_a8w4_forward calls, each "
                                  "after an untimed 1 GiB write (weights stream from HBM); step_us from HIP events "
-                                 "around each launch of the same call made through the step entry points, where "
-                                 "the top-k combine is a launch of its own (the call folds it into stage two); "
-                                 "fractions of the dense MFMA peaks (FP8 rate 5.0, FP4 10.1 PFLOP/s)"
-                                 % max(3, args.prefill_reps),
+                                 "around each launch of the same call made through the step entry points (the "
+                                 "same four launches); us_per_call_back_to_back: mean of as many calls issued "
+                                 "one after another with nothing between (the shader clock falls under that "
+                                 "sustained load); fractions of the dense MFMA peaks (FP8 rate 5.0, FP4 10.1 "
+                                 "PFLOP/s)" % max(3, args.prefill_reps),
             points=prefill)
         result["roofline_prefill"] = roof_prefill
 
@@ -718,13 +754,7 @@ def main():
                    "(%.1f s in all); mean over the buckets" % (time.perf_counter() - t_all),
             per_bucket_us=per)
     if args.calibrate_copy:
-        # a plain copy of known size: 1 GiB read + 1 GiB written per launch
-        src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
-        dst = torch.empty_like(src)
-        for _ in range(3):
-            dst.copy_(src)
-        torch.cuda.synchronize()
-        result["calibration_copy_bytes"] = 1 << 30
+        result["calibration_copy_bytes"] = calibration_copy(dev)
     print(json.dumps(result))
 
 

@@ -331,6 +331,13 @@ int moe_a16w4_stage1(const moe_a8w4_dims* dims, int32_t block_m, const void* hid
 int moe_a8w4_mfma_probe(int64_t n, int32_t byte_sel, const uint8_t* a_fp4, const uint8_t* a_scale,
                         const uint8_t* b_fp8, const uint8_t* b_scale, float* d, hipStream_t stream);
 
+/* The BF16 matrix instruction of the A16W4 variant (v_mfma_f32_16x16x32_bf16),
+ * once per 16 x 16 tile from a zero accumulator, for the same kind of
+ * measurement: a_bf16 [n, 16, 32] rows, b_bf16 [n, 16, 32] columns (BF16
+ * bits), d [n, 16, 16] float32 out = sum over K of the products.  Every
+ * pointer 16-byte aligned; 0 <= n <= 2^24. */
+int moe_a16w4_mfma_probe(int64_t n, const void* a_bf16, const void* b_bf16, float* d, hipStream_t stream);
+
 /* Name of a status code (static string). */
 const char* moe_a8w4_status_str(int status);
 

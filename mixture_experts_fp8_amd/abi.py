@@ -32,7 +32,7 @@ EXPORTS = (
     "moe_a8w4_stage1", "moe_a8w4_stage2", "moe_a8w4_combine", "moe_a8w4_status_str",
     "moe_a8w4_route", "moe_a8w4_forward_routed", "moe_a8w4_stages_fused", "moe_a8w4_fused_counters",
     "moe_a16w4_forward", "moe_a16w4_workspace_bytes", "moe_a16w4_block_m", "moe_a16w4_stage1",
-    "moe_a8w4_mfma_probe", "moe_a8w4_forward_noalloc",
+    "moe_a8w4_mfma_probe", "moe_a8w4_forward_noalloc", "moe_a16w4_mfma_probe",
 )
 
 
@@ -88,6 +88,7 @@ def load() -> ctypes.CDLL:
         "moe_a16w4_stage1": (ctypes.c_int, [P, i32] + [vp] * 7 + [vp]),
         "moe_a8w4_mfma_probe": (ctypes.c_int, [ctypes.c_int64, i32] + [vp] * 5 + [vp]),
         "moe_a8w4_forward_noalloc": (ctypes.c_int, [P] + [vp] * 8 + [vp]),
+        "moe_a16w4_mfma_probe": (ctypes.c_int, [ctypes.c_int64, vp, vp, vp, vp]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -384,4 +385,14 @@ def moe_a8w4_mfma_probe(a_fp4, a_scale, b_fp8, b_scale, byte_sel=0, d=None, stre
     st = load().moe_a8w4_mfma_probe(n, byte_sel, _ptr(a_fp4), _ptr(a_scale), _ptr(b_fp8), _ptr(b_scale),
                                     _ptr(d), _stream(stream))
     _check("moe_a8w4_mfma_probe", st)
+    return d
+
+
+def moe_a16w4_mfma_probe(a_bf16, b_bf16, d=None, stream=None):
+    """n BF16 MFMAs: a_bf16 [n,16,32], b_bf16 [n,16,32] (torch.bfloat16) -> d float32 [n,16,16]."""
+    n = a_bf16.shape[0]
+    if d is None:
+        d = torch.empty((n, 16, 16), dtype=torch.float32, device=a_bf16.device)
+    st = load().moe_a16w4_mfma_probe(n, _ptr(a_bf16), _ptr(b_bf16), _ptr(d), _stream(stream))
+    _check("moe_a16w4_mfma_probe", st)
     return d

@@ -531,6 +531,15 @@ int moe_a8w4_mfma_probe(int64_t n, int32_t byte_sel, const uint8_t* a_fp4, const
   return status_of(moe::launch_mfma_probe(n, byte_sel, a_fp4, a_scale, b_fp8, b_scale, d, stream));
 }
 
+int moe_a16w4_mfma_probe(int64_t n, const void* a_bf16, const void* b_bf16, float* d, hipStream_t stream) {
+  if (n < 0 || n > (1 << 24)) return MOE_ERR_DIMS;
+  if (n == 0) return MOE_OK;
+  if (!a_bf16 || !b_bf16 || !d) return MOE_ERR_NULL;
+  if (!all_aligned16({a_bf16, b_bf16, d})) return MOE_ERR_ALIGN;
+  return status_of(moe::launch_mfma_bf16_probe(n, static_cast<const uint16_t*>(a_bf16),
+                                               static_cast<const uint16_t*>(b_bf16), d, stream));
+}
+
 }  // extern "C"
 
 // ------------------------------------------------- the no-allocation form

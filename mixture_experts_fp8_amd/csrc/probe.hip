@@ -1,8 +1,9 @@
-// The scaled MFMA the grouped GEMMs are built from, one instruction per
-// 16 x 16 output tile, exported so that tests can measure it against exact
-// arithmetic: its operand layout, its scale-byte selection and the error of
-// its internal accumulation (which sets the local error budget of the
-// requantised intermediate).
+// The matrix instructions the grouped GEMMs are built from, one instruction
+// per 16 x 16 output tile, exported so that tests can measure them against
+// exact arithmetic: the scaled FP4 x FP8 MFMA of the A8W4 layer (operand
+// layout, scale-byte selection, the error of its internal accumulation,
+// which sets the local error budget of the requantised intermediate) and the
+// BF16 MFMA of the A16W4 variant.
 #include "gemm_common.hpp"
 
 namespace moe {
@@ -42,7 +43,30 @@ __global__ void __launch_bounds__(64) mfma_probe_kernel(const uint8_t* __restric
   for (int r = 0; r < 4; ++r) d[i * 256 + (4 * g + r) * 16 + m] = acc[r];
 }
 
+// The BF16 instruction of the A16W4 variant (v_mfma_f32_16x16x32_bf16), one
+// wave per tile i: A [16 rows][32] and B [16 cols][32] BF16, D [16][16]
+// float32 from a zero accumulator.  A lane (m, g) holds row m, K [8 g, +8);
+// B lane (n, g) column n, K [8 g, +8); D lane (n, g) column n, rows 4 g .. +3.
+__global__ void __launch_bounds__(64) mfma_bf16_probe_kernel(const uint16_t* __restrict__ a,
+                                                             const uint16_t* __restrict__ b,
+                                                             float* __restrict__ d) {
+  const int64_t i = blockIdx.x;
+  const int lane = threadIdx.x, m = lane & 15, g = lane >> 4;
+  const bf16x8 av = __builtin_bit_cast(bf16x8, *reinterpret_cast<const v4i*>(a + i * 512 + m * 32 + 8 * g));
+  const bf16x8 bv = __builtin_bit_cast(bf16x8, *reinterpret_cast<const v4i*>(b + i * 512 + m * 32 + 8 * g));
+  const v4f acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bv, v4f{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+#pragma unroll
+  for (int r = 0; r < 4; ++r) d[i * 256 + (4 * g + r) * 16 + m] = acc[r];
+}
+
 }  // namespace
+
+hipError_t launch_mfma_bf16_probe(int64_t n, const uint16_t* a, const uint16_t* b, float* d,
+                                  hipStream_t stream) {
+  if (n <= 0) return hipSuccess;
+  hipLaunchKernelGGL(mfma_bf16_probe_kernel, dim3((unsigned)n), dim3(64), 0, stream, a, b, d);
+  return hipGetLastError();
+}
 
 hipError_t launch_mfma_probe(int64_t n, int sel, const uint8_t* a, const uint8_t* as, const uint8_t* b,
                              const uint8_t* bs, float* d, hipStream_t stream) {
