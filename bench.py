@@ -66,7 +66,7 @@ def parse():
                     help="instead of the decode sweep: --steps calls of moe_a8w4_forward for one "
                          "workload and token count (a short run to put under a profiler)")
     ap.add_argument("--back-to-back", action="store_true",
-                    help="with --profile-call: no 1 GiB write between the calls")
+                    help="with --profile-call: no 1 GiB cache-evicting read between the calls")
     ap.add_argument("--local-slice-table", action="store_true",
                     help="instead of the decode sweep: one call per token count of the local-slice "
                          "workload (the pages' own MI355X fused_moe timing table) as a JSON line")
@@ -111,12 +111,12 @@ def profile_call(args):
     wd = torch.from_numpy(wts).to(dev)
     out = torch.empty((M, w.hidden), dtype=torch.bfloat16, device=dev)
     ws = torch.empty(abi.moe_a8w4_workspace_bytes(d), dtype=torch.uint8, device=dev)
-    # each call after an untimed 1 GiB write, as the prefill block times it
+    # each call after an untimed 1 GiB read that evicts the caches, as the prefill block times it
     # (--back-to-back: the calls one after another, with nothing between)
     flush = None if args.back_to_back else torch.empty(FLUSH_BYTES, dtype=torch.uint8, device=dev)
     for _ in range(args.steps):
         if flush is not None:
-            flush.zero_()
+            evict_caches(flush)
             torch.cuda._sleep(HOST_COVER_CYCLES)
         abi.moe_a8w4_forward(d, x, idd, wd, *packed, out=out, workspace=ws)
     torch.cuda.synchronize()
@@ -125,6 +125,17 @@ def profile_call(args):
         del x, out, ws, flush
         rec["calibration_copy_bytes"] = calibration_copy(dev)
     print(json.dumps(rec))
+
+
+def evict_caches(buf):
+    """Read a 1 GiB buffer (more than L2 and the 256 MB last-level cache
+    hold): afterwards those caches hold clean lines of this buffer only, so a
+    call timed next streams its weights from HBM and has no dirty lines of
+    earlier work to write back.  (A write of the buffer would leave up to the
+    last-level cache's size of dirty lines, written back inside the timed
+    call.)"""
+    import torch
+    buf.view(torch.int32).amax()
 
 
 def calibration_copy(dev):
@@ -142,7 +153,7 @@ def calibration_copy(dev):
 def local_slice_table(args):
     """Median microseconds per moe_a8w4_forward call of the local-slice workload at
     each token count of the pages' table, with algorithmic GB/s and TFLOP/s.
-    Each timed call follows an untimed 1 GiB write, so even the 1-token call
+    Each timed call follows an untimed 1 GiB read, so even the 1-token call
     (one or two experts, 12.5 MB each) streams its weights from HBM."""
     import torch
     from mixture_experts_fp8_amd import abi, workloads as wl
@@ -169,7 +180,7 @@ def local_slice_table(args):
         ts = []
         for _ in range(max(3, args.steps)):
             e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            flush.zero_()   # evicts L2 and the last-level cache: the weights stream from HBM
+            evict_caches(flush)   # the weights stream from HBM
             torch.cuda._sleep(HOST_COVER_CYCLES)   # the GPU waits while the host enqueues the call
             e0.record()
             abi.moe_a8w4_forward(d, x, idd, wd, *packed, out=out, workspace=ws)
@@ -378,13 +389,13 @@ def router_table(args):
 # local-slice geometry at its largest token count of the pages' table.
 PREFILL_POINTS = (("prefill-shared", 4096, "roundrobin"), ("prefill-shared", 16384, "roundrobin"),
                   ("prefill-shared", 16384, "softmax"), ("local-slice", 16384, "softmax"))
-FLUSH_BYTES = 1 << 30   # written before every timed prefill call: evicts L2 and the 256 MB last-level cache
+FLUSH_BYTES = 1 << 30   # read before every timed prefill call: evicts L2 and the 256 MB last-level cache
 
 
 def prefill_block(args, lib, stream):
     """Median microseconds per call at each prefill point, step by step with
     HIP events on the launch stream (the launch sequence of moe_a8w4_forward),
-    each call preceded by an untimed 1 GiB write so that the weights stream
+    each call preceded by an untimed 1 GiB read so that the weights stream
     from HBM; returns (rows, roofline of the stage-one tile kernel at the
     prefill geometry's 16384-token round-robin point)."""
     import torch
@@ -451,7 +462,7 @@ def prefill_block(args, lib, stream):
             for _ in range(max(3, args.prefill_reps)):
                 # the call as the library runs it (moe_a8w4_forward) ...
                 e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-                flush.zero_()
+                evict_caches(flush)
                 torch.cuda._sleep(HOST_COVER_CYCLES)
                 e0.record(stream)
                 if lib.moe_a8w4_forward(*a_fwd):
@@ -462,7 +473,7 @@ def prefill_block(args, lib, stream):
                 # ... and step by step through the step entry points (the
                 # combine as a launch of its own), for the per-step times
                 ev = [torch.cuda.Event(enable_timing=True) for _ in range(len(steps) + 1)]
-                flush.zero_()
+                evict_caches(flush)
                 torch.cuda._sleep(HOST_COVER_CYCLES)
                 call(ev)
                 ev[-1].synchronize()
@@ -720,7 +731,7 @@ def main():
     if prefill is not None:
         result["prefill"] = dict(
             unit="us/call", note="MFMA-bound half of the metric: median of %d moe_a8w4_forward calls, each "
-                                 "after an untimed 1 GiB write (weights stream from HBM); step_us from HIP events "
+                                 "after an untimed 1 GiB read (weights stream from HBM); step_us from HIP events "
                                  "around each launch of the same call made through the step entry points (the "
                                  "same four launches); us_per_call_back_to_back: mean of as many calls issued "
                                  "one after another with nothing between (the shader clock falls under that "
