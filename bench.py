@@ -111,14 +111,17 @@ def profile_call(args):
     wd = torch.from_numpy(wts).to(dev)
     out = torch.empty((M, w.hidden), dtype=torch.bfloat16, device=dev)
     ws = torch.empty(abi.moe_a8w4_workspace_bytes(d), dtype=torch.uint8, device=dev)
-    # each call after an untimed 1 GiB read that evicts the caches, as the prefill block times it
-    # (--back-to-back: the calls one after another, with nothing between)
+    # each call as the prefill block times it: after an untimed 1 GiB read
+    # that evicts the caches, and waited for before the next one (--back-to-back:
+    # the calls one after another, with nothing between)
     flush = None if args.back_to_back else torch.empty(FLUSH_BYTES, dtype=torch.uint8, device=dev)
     for _ in range(args.steps):
         if flush is not None:
             evict_caches(flush)
             torch.cuda._sleep(HOST_COVER_CYCLES)
         abi.moe_a8w4_forward(d, x, idd, wd, *packed, out=out, workspace=ws)
+        if flush is not None:
+            torch.cuda.synchronize()
     torch.cuda.synchronize()
     rec = {"profile_call": args.profile_call, "calls": args.steps, "back_to_back": args.back_to_back}
     if args.calibrate_copy:
