@@ -176,8 +176,8 @@ def test_edge_cases():
 @pytest.mark.parametrize("E,M,want_bm", [(16, 80, 32), (16, 200, 64), (8, 400, 128)])
 def test_steps_compose_to_forward(E, M, want_bm):
     """The step entry points (stage two writing route rows, then the separate
-    combine) give the forward's output bit for bit, whether the forward runs
-    the separate combine (blocks of 16/32) or folds it into stage two (64/128)."""
+    combine) give the forward's output bit for bit, at blocks of 32, 64 and
+    128 routes."""
     w = wl.scaled(wl.WORKLOADS["draft-sweep"], num_experts=E, routed_experts=E, config_id=121)
     layer = Layer(w)
     hidden, ids, wts = wl.make_inputs(w, M, "softmax")
@@ -203,6 +203,72 @@ def test_steps_compose_to_forward(E, M, want_bm):
     assert torch.equal(out_steps.view(torch.int16), out_fwd.view(torch.int16))
     assert torch.equal(out_again.view(torch.int16), out_fwd.view(torch.int16))
     check_forward(layer, hidden, ids, wts, host_bf16_bits(out_fwd), xd, idd)
+
+
+def shared_layer():
+    """A small layer with the prefill configuration's fused shared expert:
+    8 routed experts top-2 plus the shared one (local expert 8) in the last
+    slot, I = 640."""
+    w = wl.scaled(wl.WORKLOADS["prefill-shared"], hidden=1024, num_experts=9, routed_experts=8, topk=3,
+                  config_id=901)
+    return w, Layer(w)
+
+
+def edit_shared_routes(w, ids, duplicates):
+    """Tokens that break the shared-expert pattern: no shared slot, the
+    shared expert twice, the shared expert first, only the shared slot local,
+    no local slot, an out-of-range routed id; `duplicates` more tokens with
+    the shared expert in two slots."""
+    x = w.routed_experts
+    ids = ids.copy()
+    ids[0, 2] = (ids[0, 0] + 1) % x if (ids[0, 0] + 1) % x != ids[0, 1] else (ids[0, 0] + 2) % x
+    ids[1, 0] = x
+    ids[2, [0, 2]] = ids[2, [2, 0]]
+    ids[3, :2] = -1
+    ids[4, :] = -1
+    ids[5, 1] = 500
+    ids[6:6 + duplicates, 1] = x
+    return ids
+
+
+@pytest.mark.parametrize("M,duplicates", [(20, 0), (40, 0), (100, 0), (400, 0), (400, 150), (40, 30), (20, 12)])
+def test_shared_expert_routes(M, duplicates):
+    """The prefill configuration's fused shared expert, with tokens that
+    break its pattern (no shared slot, the shared expert twice or first, only
+    the shared slot local, none local, an out-of-range id) and with many
+    tokens holding it twice (its sorted run then longer than M): at every
+    block size moe_a8w4_forward gives the step entry points' output bit for
+    bit, repeatably, zeros for the token with no local slot, and the
+    oracle's gate on every token."""
+    w, layer = shared_layer()
+    hidden, ids, wts = wl.make_inputs(w, M, "softmax")
+    ids = edit_shared_routes(w, ids, duplicates)
+    d = layer.dims(M)
+    bm = abi.moe_a8w4_block_m(d)
+    note("shared-expert routes M=%d bm=%d duplicates=%d" % (M, bm, duplicates))
+    xd, idd, wd = dev(hidden), dev(ids), dev(wts)
+    q, s = abi.moe_a8w4_quant_act(xd)
+    srt, bexp, npad = abi.moe_a8w4_sort(d, bm, idd)
+    iq, is_ = abi.moe_a8w4_stage1(d, bm, q, s, srt, bexp, npad, layer.packed[0], layer.packed[1])
+    y = abi.moe_a8w4_stage2(d, bm, iq, is_, srt, bexp, npad, wd, layer.packed[2], layer.packed[3])
+    out_steps = abi.moe_a8w4_combine(d, idd, y)
+    out_fwd = torch.full((M, w.hidden), float("nan"), dtype=torch.bfloat16, device=DEV)
+    layer.forward(xd, idd, wd, out=out_fwd)
+    out_again = layer.forward(xd, idd, wd)
+    torch.cuda.synchronize()
+    assert torch.equal(out_steps.view(torch.int16), out_fwd.view(torch.int16))
+    assert torch.equal(out_again.view(torch.int16), out_fwd.view(torch.int16))
+    bits = host_bf16_bits(out_fwd)
+    assert np.all(bits[4] == 0)
+    check_forward(layer, hidden, ids, wts, bits, xd, idd)
+
+
+def test_shared_expert_block_sizes_covered():
+    """The token counts of test_shared_expert_routes reach every block size."""
+    w, _ = shared_layer()
+    bms = {abi.moe_a8w4_block_m(abi.make_dims(M, w.hidden, w.inter, w.num_experts, w.topk, w.expert_offset,
+                                               w.routed_experts)) for M in (20, 40, 100, 400)}
+    assert bms == {16, 32, 64, 128}
 
 
 def test_graph_replay_on_changed_inputs():
