@@ -218,51 +218,64 @@ __global__ void __launch_bounds__(64 * (kComputeWaves + kLoaderWaves), 3) tile_k
         dma4(args.bs + row * (K / 32) + 4 * (d - u * KS), pre0 + (uint32_t)d0 * 4);
       }
     }
-    auto issue = [&](int s) {
-      const uint32_t base = lds0 + (uint32_t)(s % S) * G::BYTES;
+    // A block's routes come first and its padding last, so when the first
+    // token of this loader's chunks is padding all of them are: their rows
+    // feed only output columns that are never stored, and their loads are
+    // skipped (a block of 128 routes holding 64 reads half the token bytes).
+    const bool skip_tok = ids[8 * l * G::NBCH] == M;
+    auto run_loader = [&](auto skip_tag) {
+      constexpr bool SKIP = decltype(skip_tag)::value;
+      constexpr int LOADS = G::LOADS - (SKIP ? G::NBCH : 0);
+      auto issue = [&](int s) {
+        const uint32_t base = lds0 + (uint32_t)(s % S) * G::BYTES;
 #pragma unroll
-      for (int t = 0; t < 4; ++t)
-        dma16(gA + (int64_t)s * 4096 + t * 1024, base + G::A + l * 4096 + t * 1024);
+        for (int t = 0; t < 4; ++t)
+          dma16(gA + (int64_t)s * 4096 + t * 1024, base + G::A + l * 4096 + t * 1024);
+        if constexpr (!SKIP) {
 #pragma unroll
-      for (int i = 0; i < G::NBCH; ++i) dma16(gB[i] + s * 128, base + G::B + (l * G::NBCH + i) * 1024);
-      dma4(gAs + (int64_t)s * 256, base + G::AS + l * 256);
-      if (has_bs) {
-        if constexpr (SC4) {
-          if ((s & 3) == 0) dma16(gBs + 4 * s, lds_addr(&ssc[0]) + (uint32_t)((s >> 2) & 1) * (BM * 16) + l * 1024);
-        } else {
-          dma4(gBs + 4 * s, base + G::BS + l * 256);
+          for (int i = 0; i < G::NBCH; ++i) dma16(gB[i] + s * 128, base + G::B + (l * G::NBCH + i) * 1024);
         }
-      }
-    };
-#pragma unroll
-    for (int s = 0; s < S - 1; ++s)
-      if (s < KS) issue(s);
-    for (int s = 0; s < KS; ++s) {
-      // barrier s publishes step s: it has landed once at most the loads of
-      // steps s+1 .. s+S-2 are outstanding (near the end: none)
-      if (s + S - 2 < KS) {
+        dma4(gAs + (int64_t)s * 256, base + G::AS + l * 256);
         if (has_bs) {
           if constexpr (SC4) {
-            // steps s+1 .. s+S-2 (at most 3 of them) hold at most one
-            // scale load, the one of a step that is a multiple of 4
-            bool sc = false;
-#pragma unroll
-            for (int j = 1; j <= S - 2; ++j) sc = sc || ((s + j) & 3) == 0;
-            if (sc) __builtin_amdgcn_s_waitcnt(vmcnt_only((S - 2) * G::LOADS + 1));
-            else __builtin_amdgcn_s_waitcnt(vmcnt_only((S - 2) * G::LOADS));
+            if ((s & 3) == 0) dma16(gBs + 4 * s, lds_addr(&ssc[0]) + (uint32_t)((s >> 2) & 1) * (BM * 16) + l * 1024);
           } else {
-            __builtin_amdgcn_s_waitcnt(vmcnt_only((S - 2) * (G::LOADS + 1)));
+            dma4(gBs + 4 * s, base + G::BS + l * 256);
+          }
+        }
+      };
+#pragma unroll
+      for (int s = 0; s < S - 1; ++s)
+        if (s < KS) issue(s);
+      for (int s = 0; s < KS; ++s) {
+        // barrier s publishes step s: it has landed once at most the loads of
+        // steps s+1 .. s+S-2 are outstanding (near the end: none)
+        if (s + S - 2 < KS) {
+          if (has_bs) {
+            if constexpr (SC4) {
+              // steps s+1 .. s+S-2 (at most 3 of them) hold at most one
+              // scale load, the one of a step that is a multiple of 4
+              bool sc = false;
+#pragma unroll
+              for (int j = 1; j <= S - 2; ++j) sc = sc || ((s + j) & 3) == 0;
+              if (sc) __builtin_amdgcn_s_waitcnt(vmcnt_only((S - 2) * LOADS + 1));
+              else __builtin_amdgcn_s_waitcnt(vmcnt_only((S - 2) * LOADS));
+            } else {
+              __builtin_amdgcn_s_waitcnt(vmcnt_only((S - 2) * (LOADS + 1)));
+            }
+          } else {
+            __builtin_amdgcn_s_waitcnt(vmcnt_only((S - 2) * LOADS));
           }
         } else {
-          __builtin_amdgcn_s_waitcnt(vmcnt_only((S - 2) * G::LOADS));
+          __builtin_amdgcn_s_waitcnt(vmcnt_only(0));
         }
-      } else {
-        __builtin_amdgcn_s_waitcnt(vmcnt_only(0));
+        barrier_only();
+        // every compute wave has finished reading step s - 1: refill its slot
+        if (s + S - 1 < KS) issue(s + S - 1);
       }
-      barrier_only();
-      // every compute wave has finished reading step s - 1: refill its slot
-      if (s + S - 1 < KS) issue(s + S - 1);
-    }
+    };
+    if (skip_tok) run_loader(std::true_type{});
+    else run_loader(std::false_type{});
     return;
   }
 
