@@ -61,6 +61,20 @@ __device__ __forceinline__ void dma16(const void* g, uint32_t lds) {
   asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(g), "s"(lds)
                : "memory", "m0");
 }
+// The same with the non-temporal hint, for weights that stage two streams
+// past the caches (each 256-row slice of an expert is read by the few blocks
+// of that expert, side by side; measured faster than cached loads for every
+// prefill stage-two shape, e.g. prefill-shared 4096 tokens 274 -> 251 us,
+// local slice 16384 tokens 383 -> 361 us).
+__device__ __forceinline__ void dma16nt(const void* g, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off nt" ::"v"(g), "s"(lds)
+               : "memory", "m0");
+}
+template <int STAGE>
+__device__ __forceinline__ void dma16w(const void* g, uint32_t lds) {
+  if constexpr (STAGE == 2) dma16nt(g, lds);
+  else dma16(g, lds);
+}
 __device__ __forceinline__ void dma4(const void* g, uint32_t lds) {
   asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dword %0, off" ::"v"(g), "s"(lds)
                : "memory", "m0");
@@ -230,7 +244,7 @@ __global__ void __launch_bounds__(64 * (kComputeWaves + kLoaderWaves), 3) tile_k
         const uint32_t base = lds0 + (uint32_t)(s % S) * G::BYTES;
 #pragma unroll
         for (int t = 0; t < 4; ++t)
-          dma16(gA + (int64_t)s * 4096 + t * 1024, base + G::A + l * 4096 + t * 1024);
+          dma16w<STAGE>(gA + (int64_t)s * 4096 + t * 1024, base + G::A + l * 4096 + t * 1024);
         if constexpr (!SKIP) {
 #pragma unroll
           for (int i = 0; i < G::NBCH; ++i) dma16(gB[i] + s * 128, base + G::B + (l * G::NBCH + i) * 1024);
@@ -515,7 +529,7 @@ __global__ void __launch_bounds__(64 * (kComputeWaves + kLoaderWaves), 3) tile_r
       const int64_t step = (int64_t)j * 4 * KS + ks;   // row group advances by 4 per slice
       const uint32_t base = lds0 + (uint32_t)(q % S) * SLOT;
 #pragma unroll
-      for (int t = 0; t < 4; ++t) dma16(gA + step * 4096 + t * 1024, base + l * 4096 + t * 1024);
+      for (int t = 0; t < 4; ++t) dma16w<STAGE>(gA + step * 4096 + t * 1024, base + l * 4096 + t * 1024);
       dma4(gAs + step * 256, base + 16384 + l * 256);
     };
 #pragma unroll
