@@ -75,6 +75,9 @@ def parse():
                          "against the fused decode launch")
     ap.add_argument("--a16w4-table", action="store_true",
                     help="instead of the decode sweep: the A16W4 variant at the pages' A16W4 sizes")
+    ap.add_argument("--layout-probe", action="store_true",
+                    help="instead of the decode sweep: stream the backbone stage-one weights in the "
+                         "decode kernel's shape from the packed and from the raw row-major layout")
     ap.add_argument("--router-table", action="store_true",
                     help="instead of the decode sweep: per backbone decode bucket, the router alone, "
                          "the layer from given routes and the layer from router logits (JSON line)")
@@ -139,6 +142,41 @@ def evict_caches(buf):
     call.)"""
     import torch
     buf.view(torch.int32).amax()
+
+
+def layout_probe(args):
+    """GB/s of moe_a8w4_stream_probe over the backbone's stage-one weights
+    (384 experts x 1280 rows x K 5120, E2M1 codes and E8M0 scales) in the
+    packed layout and in the raw row-major one: median of 10 launches, each
+    after the 1 GiB cache-evicting read."""
+    import torch
+    from mixture_experts_fp8_amd import abi
+    dev = torch.device("cuda:0")
+    rows, K = 384 * 1280, 5120
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(7)
+    codes = torch.randint(0, 256, (rows * K // 2,), dtype=torch.uint8, device=dev, generator=gen)
+    scales = torch.randint(118, 123, (rows * K // 32,), dtype=torch.uint8, device=dev, generator=gen)
+    out = torch.empty(rows // 64 * 4, dtype=torch.int32, device=dev)
+    flush = torch.empty(FLUSH_BYTES, dtype=torch.uint8, device=dev)
+    nbytes = codes.numel() + scales.numel()
+    res = {}
+    for layout, name in ((0, "packed"), (1, "raw")):
+        abi.moe_a8w4_stream_probe(layout, rows, K, codes, scales, out=out)
+        ts = []
+        for _ in range(10):
+            evict_caches(flush)
+            torch.cuda._sleep(HOST_COVER_CYCLES)
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            abi.moe_a8w4_stream_probe(layout, rows, K, codes, scales, out=out)
+            e1.record()
+            e1.synchronize()
+            ts.append(e0.elapsed_time(e1) * 1e3)
+        us = float(np.median(ts))
+        res[name] = dict(us=round(us, 1), GBps=round(nbytes / us / 1e3, 1))
+        print("%s layout: %.1f us, %.1f GB/s" % (name, us, nbytes / us / 1e3), file=sys.stderr, flush=True)
+    print(json.dumps({"probe": "weight streaming, decode stage-one shape", "bytes": nbytes, "layouts": res}))
 
 
 def calibration_copy(dev):
@@ -588,6 +626,9 @@ def main():
         return
     if args.profile_call:
         profile_call(args)
+        return
+    if args.layout_probe:
+        layout_probe(args)
         return
     dev = torch.device("cuda:0")
     lib = abi.load()

@@ -109,8 +109,9 @@ int64_t moe_a8w4_sort_capacity(const moe_a8w4_dims* dims, int32_t block_m);
  * one E8M0 scale per 32 along K, gate and up rows interleaved).  Packing is a
  * permutation of bytes, so the layer computes exactly what it would on the
  * raw layout; reading the raw layout in the order the matrix instruction
- * wants instead streams at 2.4 TB/s against 6.7 TB/s (measured, decode stage
- * one).  Inputs, row-major, element 2i in the low nibble of byte i:
+ * wants instead streams at 3.1 TB/s against 6.8 TB/s (measured in the decode
+ * stage-one shape: moe_a8w4_stream_probe).  Inputs, row-major, element 2i in
+ * the low nibble of byte i:
  *   w13      [E, 2I, H/2]  E2M1 codes; row 2j = gate of column j, row 2j+1 = up
  *   w13_s    [E, 2I, H/32] E8M0 scale of each run of 32 elements along H
  *   w2       [E, H, I/2]   E2M1 codes
@@ -337,6 +338,19 @@ int moe_a8w4_mfma_probe(int64_t n, int32_t byte_sel, const uint8_t* a_fp4, const
  * bits), d [n, 16, 16] float32 out = sum over K of the products.  Every
  * pointer 16-byte aligned; 0 <= n <= 2^24. */
 int moe_a16w4_mfma_probe(int64_t n, const void* a_bf16, const void* b_bf16, float* d, hipStream_t stream);
+
+/* Weight streaming in the shape of the decode stage-one kernel, for the
+ * measurement behind the packed layout of moe_a8w4_pack_weights: one
+ * workgroup per 64-row group of `rows` rows of K, 4 waves splitting K, every
+ * lane loading one MFMA tile's A operand per K step with non-temporal 16-byte
+ * loads, from the packed layout (layout 0: w, w_s as moe_a8w4_pack_weights
+ * writes them for rows x K) or from the raw row-major one (layout 1: w
+ * [rows, K/2], w_s [rows, K/32]).  out [rows / 64 * 4] uint32 receives one
+ * fold of the loaded bytes per wave; raw weights and their packed form give
+ * the same words.  rows a multiple of 64, K of 512; 16-byte aligned
+ * pointers. */
+int moe_a8w4_stream_probe(int32_t layout, int64_t rows, int32_t K, const uint8_t* w, const uint8_t* w_s,
+                          uint32_t* out, hipStream_t stream);
 
 /* Name of a status code (static string). */
 const char* moe_a8w4_status_str(int status);

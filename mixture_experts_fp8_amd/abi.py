@@ -32,7 +32,7 @@ EXPORTS = (
     "moe_a8w4_stage1", "moe_a8w4_stage2", "moe_a8w4_combine", "moe_a8w4_status_str",
     "moe_a8w4_route", "moe_a8w4_forward_routed", "moe_a8w4_stages_fused", "moe_a8w4_fused_counters",
     "moe_a16w4_forward", "moe_a16w4_workspace_bytes", "moe_a16w4_block_m", "moe_a16w4_stage1",
-    "moe_a8w4_mfma_probe", "moe_a8w4_forward_noalloc", "moe_a16w4_mfma_probe",
+    "moe_a8w4_mfma_probe", "moe_a8w4_forward_noalloc", "moe_a16w4_mfma_probe", "moe_a8w4_stream_probe",
 )
 
 
@@ -89,6 +89,7 @@ def load() -> ctypes.CDLL:
         "moe_a8w4_mfma_probe": (ctypes.c_int, [ctypes.c_int64, i32] + [vp] * 5 + [vp]),
         "moe_a8w4_forward_noalloc": (ctypes.c_int, [P] + [vp] * 8 + [vp]),
         "moe_a16w4_mfma_probe": (ctypes.c_int, [ctypes.c_int64, vp, vp, vp, vp]),
+        "moe_a8w4_stream_probe": (ctypes.c_int, [ctypes.c_int32, ctypes.c_int64, ctypes.c_int32, vp, vp, vp, vp]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -396,3 +397,12 @@ def moe_a16w4_mfma_probe(a_bf16, b_bf16, d=None, stream=None):
     st = load().moe_a16w4_mfma_probe(n, _ptr(a_bf16), _ptr(b_bf16), _ptr(d), _stream(stream))
     _check("moe_a16w4_mfma_probe", st)
     return d
+
+
+def moe_a8w4_stream_probe(layout, rows, K, w, w_s, out=None, stream=None):
+    """Weight-streaming probe: layout 0 packed, 1 raw row-major; out uint32 [rows / 64 * 4]."""
+    if out is None:
+        out = torch.empty(rows // 64 * 4, dtype=torch.int32, device=w.device)
+    st = load().moe_a8w4_stream_probe(layout, rows, K, _ptr(w), _ptr(w_s), _ptr(out), _stream(stream))
+    _check("moe_a8w4_stream_probe", st)
+    return out

@@ -531,6 +531,17 @@ int moe_a8w4_mfma_probe(int64_t n, int32_t byte_sel, const uint8_t* a_fp4, const
   return status_of(moe::launch_mfma_probe(n, byte_sel, a_fp4, a_scale, b_fp8, b_scale, d, stream));
 }
 
+int moe_a8w4_stream_probe(int32_t layout, int64_t rows, int32_t K, const uint8_t* w, const uint8_t* w_s,
+                          uint32_t* out, hipStream_t stream) {
+  if ((layout != 0 && layout != 1) || rows < 0 || rows % 64 || rows > ((int64_t)1 << 28) || K <= 0 ||
+      K % 512 || K > (1 << 16))
+    return MOE_ERR_DIMS;
+  if (rows == 0) return MOE_OK;
+  if (!w || !w_s || !out) return MOE_ERR_NULL;
+  if (!all_aligned16({w, w_s, out})) return MOE_ERR_ALIGN;
+  return status_of(moe::launch_stream_probe(layout, rows / 64, K, w, w_s, out, stream));
+}
+
 int moe_a16w4_mfma_probe(int64_t n, const void* a_bf16, const void* b_bf16, float* d, hipStream_t stream) {
   if (n < 0 || n > (1 << 24)) return MOE_ERR_DIMS;
   if (n == 0) return MOE_OK;

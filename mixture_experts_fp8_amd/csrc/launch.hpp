@@ -87,6 +87,10 @@ hipError_t launch_tile(int stage, const GemmArgs& a, int64_t max_blocks, hipStre
 // n independent 16 x 16 scaled MFMAs, A scale as byte sel of its operand (probe.hip)
 hipError_t launch_mfma_probe(int64_t n, int sel, const uint8_t* a, const uint8_t* as, const uint8_t* b,
                              const uint8_t* bs, float* d, hipStream_t stream);
+// weight streaming in the decode stage-one shape, packed (layout 0) or raw
+// row-major (1) MXFP4 weights of groups * 64 rows x K (probe.hip)
+hipError_t launch_stream_probe(int layout, int64_t groups, int K, const uint8_t* w, const uint8_t* ws,
+                               uint32_t* out, hipStream_t stream);
 // n independent 16 x 16 x 32 BF16 MFMAs (probe.hip)
 hipError_t launch_mfma_bf16_probe(int64_t n, const uint16_t* a, const uint16_t* b, float* d,
                                   hipStream_t stream);

@@ -3,7 +3,8 @@
 // exact arithmetic: the scaled FP4 x FP8 MFMA of the A8W4 layer (operand
 // layout, scale-byte selection, the error of its internal accumulation,
 // which sets the local error budget of the requantised intermediate) and the
-// BF16 MFMA of the A16W4 variant.
+// BF16 MFMA of the A16W4 variant; and the weight-streaming probe behind the
+// packed weight layout.
 #include "gemm_common.hpp"
 
 namespace moe {
@@ -59,7 +60,59 @@ __global__ void __launch_bounds__(64) mfma_bf16_probe_kernel(const uint16_t* __r
   for (int r = 0; r < 4; ++r) d[i * 256 + (4 * g + r) * 16 + m] = acc[r];
 }
 
+// Weight streaming in the decode stage-one kernel's shape (one workgroup per
+// 64-row group, 4 waves splitting K, non-temporal 16-byte loads, every lane
+// loading exactly the A operand of one MFMA tile per K step), from the
+// packed layout of moe_a8w4_pack_weights (1 KB contiguous per instruction)
+// or from the raw row-major MXFP4 layout [rows, K/2] (each instruction 16
+// rows x 64 B).  Lane (m, q) of tile t at step s holds row
+// 64 G + pack_row(t, m), K [128 s + 32 q, +32), and the tile's E8M0 scale
+// as byte t of one word, in both kernels; each lane folds what it loads into
+// one word, and a wave writes that word of lane 0 ... 63 summed: for raw
+// weights and their packed form the two kernels write the same words.
+template <bool PACKED>
+__global__ void __launch_bounds__(256) stream_probe_kernel(const uint8_t* __restrict__ w,
+                                                           const uint8_t* __restrict__ ws, int K,
+                                                           uint32_t* __restrict__ out) {
+  const int64_t G = blockIdx.x;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, m = lane & 15, q = lane >> 4;
+  const int KS = K / 128;
+  const int s0 = wave * KS / 4, s1 = (wave + 1) * KS / 4;
+  uint32_t acc = 0;
+  for (int s = s0; s < s1; ++s) {
+    v4i a[4];
+    uint32_t sc = 0;
+    if constexpr (PACKED) {
+      const uint8_t* base = w + (G * KS + s) * 4096 + lane * 16;
+#pragma unroll
+      for (int t = 0; t < 4; ++t) a[t] = __builtin_nontemporal_load(reinterpret_cast<const v4i*>(base + t * 1024));
+      sc = __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(ws + ((G * KS + s) * 64 + lane) * 4));
+    } else {
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        const int64_t row = G * 64 + pack_row(t, m);
+        a[t] = __builtin_nontemporal_load(reinterpret_cast<const v4i*>(w + row * (K / 2) + 64 * s + 16 * q));
+        sc |= (uint32_t)ws[row * (K / 32) + 4 * s + q] << (8 * t);
+      }
+    }
+    acc += (uint32_t)(a[0].x ^ a[1].y ^ a[2].z ^ a[3].w) + sc;
+  }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) acc += __shfl_xor(acc, o);
+  if (lane == 0) out[G * 4 + wave] = acc;
+}
+
 }  // namespace
+
+hipError_t launch_stream_probe(int layout, int64_t groups, int K, const uint8_t* w, const uint8_t* ws,
+                               uint32_t* out, hipStream_t stream) {
+  if (groups <= 0) return hipSuccess;
+  if (layout == 0)
+    hipLaunchKernelGGL(stream_probe_kernel<true>, dim3((unsigned)groups), dim3(256), 0, stream, w, ws, K, out);
+  else
+    hipLaunchKernelGGL(stream_probe_kernel<false>, dim3((unsigned)groups), dim3(256), 0, stream, w, ws, K, out);
+  return hipGetLastError();
+}
 
 hipError_t launch_mfma_bf16_probe(int64_t n, const uint16_t* a, const uint16_t* b, float* d,
                                   hipStream_t stream) {

@@ -233,6 +233,12 @@ def test_mfma_probe_validates():
     assert lib.moe_a8w4_mfma_probe(-1, 0, p, p, p, p, p, None) == abi.MOE_ERR_DIMS
     assert lib.moe_a8w4_mfma_probe(1, 0, p, None, p, p, p, None) == abi.MOE_ERR_NULL
     assert lib.moe_a8w4_mfma_probe(1, 0, ctypes.c_void_p((1 << 20) + 8), p, p, p, p, None) == abi.MOE_ERR_ALIGN
+    assert lib.moe_a8w4_stream_probe(0, 0, 512, None, None, None, None) == abi.MOE_OK
+    assert lib.moe_a8w4_stream_probe(2, 64, 512, p, p, p, None) == abi.MOE_ERR_DIMS
+    assert lib.moe_a8w4_stream_probe(0, 65, 512, p, p, p, None) == abi.MOE_ERR_DIMS
+    assert lib.moe_a8w4_stream_probe(1, 64, 384, p, p, p, None) == abi.MOE_ERR_DIMS
+    assert lib.moe_a8w4_stream_probe(1, 64, 512, p, None, p, None) == abi.MOE_ERR_NULL
+    assert lib.moe_a8w4_stream_probe(0, 64, 512, p, p, ctypes.c_void_p((1 << 20) + 4), None) == abi.MOE_ERR_ALIGN
     assert lib.moe_a16w4_mfma_probe(0, None, None, None, None) == abi.MOE_OK
     assert lib.moe_a16w4_mfma_probe(-1, p, p, p, None) == abi.MOE_ERR_DIMS
     assert lib.moe_a16w4_mfma_probe((1 << 24) + 1, p, p, p, None) == abi.MOE_ERR_DIMS
