@@ -726,7 +726,7 @@ __global__ void __launch_bounds__(64 * (kComputeWaves + kLoaderWaves), 3) a16_ti
       const uint32_t base = lds0 + (uint32_t)(s % S) * G::BYTES;
 #pragma unroll
       for (int t = 0; t < 4; ++t)
-        dma16(gA + (int64_t)s * 4096 + t * 1024, base + G::A + l * 4096 + t * 1024);
+        dma16w<STAGE>(gA + (int64_t)s * 4096 + t * 1024, base + G::A + l * 4096 + t * 1024);
 #pragma unroll
       for (int i = 0; i < G::NBCH; ++i) dma16(gB[i] + s * 256, base + G::B + (l * G::NBCH + i) * 1024);
       dma4(gAs + (int64_t)s * 256, base + G::AS + l * 256);
