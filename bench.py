@@ -604,7 +604,7 @@ def algorithmic(w, M, ids):
 def main():
     args = parse()
     if args.gpus != 1:
-        print("bench.py runs on one GPU: this build has no multi-GPU path "
+        print("bench.py runs on one GPU: the library has no multi-GPU path "
               "(the layer is measured on one GPU's share of the experts).", file=sys.stderr)
         sys.exit(2)
 

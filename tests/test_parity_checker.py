@@ -55,7 +55,7 @@ def test_oracle_results_pass(case):
     assert rates["code_flips"] == 0 and rates["e2e_miss"] == 0 and rates["tokens"] == 24
 
 
-def test_chunking_does_not_change_the_verdict(case, monkeypatch):
+def test_chunking_does_not_change_the_outcome(case, monkeypatch):
     layer, res = case
     monkeypatch.setattr(gpu_util, "ROUTES_PER_CHUNK", 7)
     assert run(layer, res)["tokens"] == 24
