@@ -7,7 +7,8 @@ the oracle uses FP64, and rounds its own SiLU(g) * u to BF16, so an element
 may land one BF16 step away from the oracle's.  It must lie within the
 accumulation budget (2^-16 of the sum of |x w| over K, propagated through
 SiLU(g) * u) plus one BF16 step (2^-7 relative) of the oracle's exact FP64
-value, and at most 1 % of the elements may differ from the oracle's BF16.
+value, and at most 1e-3 of the elements (at least 4) may differ from the
+oracle's BF16.
 The output: every element within atol = rtol = 2e-2 of the oracle's (the
 pages' per-rank gate) and finite."""
 import numpy as np
@@ -20,6 +21,10 @@ from mixture_experts_fp8_amd import abi, workloads as wl
 from gpu_util import DEV, Layer, assert_gate, dev, host_bf16_bits, log_rates, note
 
 pytestmark = pytest.mark.gpu
+
+# fraction of BF16 intermediate values allowed to differ from the oracle's
+# (measured 1.3e-4 .. 2.2e-4 at full size; at least 4 allowed in tiny cases)
+MAX_A16_FLIPS = 1e-3
 
 
 def a16_forward(layer, hidden, ids, wts, out=None):
@@ -76,7 +81,8 @@ def test_a16_stage1_intermediate(name, E, routed, M):
             t, k, (err - dh - 2.0 ** -7 * np.abs(h64)).max())
         flips += int((got[p] != hb).sum())
         total += hb.size
-    assert flips <= 0.01 * total, "%d of %d intermediate values differ from the oracle's BF16" % (flips, total)
+    assert flips <= max(4, MAX_A16_FLIPS * total), "%d of %d intermediate values differ from the oracle's BF16" % (
+        flips, total)
 
 
 @pytest.mark.parametrize("name,E,routed,M", SMALL + [("a16w4-backbone", 16, 64, 20)])
@@ -133,13 +139,13 @@ def a16_row_max(layer):
     return layer._a16_row_max
 
 
-def check_a16_every_token(L, hidden, ids, wts, got_bits, xd, idd, max_flips=0.01, max_e2e_miss=3e-3):
+def check_a16_every_token(L, hidden, ids, wts, got_bits, xd, idd, max_flips=None, max_e2e_miss=1e-3):
     """The A16W4 layer against the oracle on every token, in three parts:
     (a) the GPU's BF16 intermediate (its stage-one launch) within the FP32
         accumulation budget (2^-16 of max|w_row| * sum|x|, a bound on
         2^-16 sum|x w|, propagated through SiLU(g) * u) plus one BF16 step of
         the oracle's exact value, at most max_flips of the values differing
-        from the oracle's BF16;
+        from the oracle's BF16 (default MAX_A16_FLIPS, and at least 4);
     (b) given that intermediate, the output at the gate on every element;
     (c) end to end, every element outside the gate belongs to a token with a
         differing intermediate value, at most max_e2e_miss of them."""
@@ -210,7 +216,8 @@ def check_a16_every_token(L, hidden, ids, wts, got_bits, xd, idd, max_flips=0.01
     note("  a16 parity: %d tokens, intermediate BF16 flips %.2e, end-to-end outside gate %.2e" % (
         M, rates["flips"], rates["e2e_miss"]))
     log_rates("a16w4", rates)
-    assert rates["flips"] <= max_flips and rates["e2e_miss"] <= max_e2e_miss, rates
+    cap = MAX_A16_FLIPS if max_flips is None else max_flips
+    assert flips <= max(4, cap * vals) and rates["e2e_miss"] <= max_e2e_miss, rates
     return rates
 
 
