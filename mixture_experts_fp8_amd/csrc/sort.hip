@@ -17,7 +17,7 @@
 // dropped.
 //
 // The routes are cut into NS contiguous chunks, one workgroup of 16 waves
-// per chunk (NS = 1 up to 4096 routes).  Every workgroup counts all routes per
+// per chunk (NS = 1 up to 1024 routes, at most 64).  Every workgroup counts all routes per
 // expert (so each knows every expert's padded start and how many of the
 // expert's routes lie in earlier chunks; no data passes between workgroups),
 // then places its own chunk.  Wave w of a workgroup owns the contiguous
@@ -26,12 +26,21 @@
 //      (LDS atomics; counts only);
 //   2. one scan gives every expert its padded start and every (wave, expert)
 //      the position of that wave's first route of the expert;
-//   3. each wave walks its routes 64 at a time; the lanes holding the same
+//   3. the padding and block experts.  At blocks of 16 (at most 15 padding
+//      entries per expert) one lane per expert writes them.  At larger
+//      blocks one wave per expert does, its lanes on consecutive positions,
+//      the experts spread over every workgroup's waves: one lane per expert
+//      writing up to block_m - 1 entries one at a time makes every store
+//      touch 64 scattered lines (the sort of 28,672 routes in blocks of 128
+//      took 25 us that way, 12 us with the per-wave stores).  At blocks of
+//      16 the per-wave loop (up to 24 experts per wave in one workgroup) is
+//      the slower one;
+//   4. each wave walks its routes 64 at a time; the lanes holding the same
 //      expert are found with one ballot per bit of the expert id, and the
 //      rank of a route among them is a popcount of that lane mask, so no
 //      barrier or atomic ordering is involved and the result is
 //      deterministic.
-// Workgroup 0 also writes the padding, the block experts and num_padded.
+// Workgroup 0 also writes num_padded.
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -42,7 +51,7 @@ namespace {
 constexpr int kPrepThreads = 1024;
 constexpr int kSortWaves = kPrepThreads / kWave;
 
-constexpr int kRoutesPerSortBlock = 4096;
+constexpr int kRoutesPerSortBlock = 1024;
 constexpr int kMaxSortBlocks = 64;
 
 struct SortSmem {
@@ -154,15 +163,35 @@ __device__ void sort_chunk(SortSmem& sm, const int32_t* ids, int M, int topk, in
       sm.cnt[j][tid] = run;
       run += n;
     }
-    if (chunk == 0) {
-      for (int p = start + c; p < start + pc; ++p) sorted_ids[p] = M;
-      for (int b = start / bm; b < (start + pc) / bm; ++b) block_expert[b] = tid;
+    if (bm <= 16) {
+      // blocks of 16: at most 15 padding entries, one lane per expert
+      if (chunk == 0) {
+        for (int p = start + c; p < start + pc; ++p) sorted_ids[p] = M;
+        for (int b = start / bm; b < (start + pc) / bm; ++b) block_expert[b] = tid;
+      }
+    } else {
+      // only this thread reads these two entries: they now hold the
+      // expert's padded start and its route count
+      sm.before[tid] = start;
+      sm.after[tid] = c;
     }
   }
   if (chunk == 0 && tid == 0) *num_padded = total;
   __syncthreads();
 
-  // 3. each wave places its own routes in order; only wave-private LDS is used
+  // 3. (blocks of 32 and more) the padding and the block experts: one wave
+  // per expert, its lanes on consecutive positions (whole-line stores), the
+  // experts spread over the waves of every sort workgroup
+  if (bm > 16) {
+    for (int e = chunk * kSortWaves + w; e < E; e += nchunks * kSortWaves) {
+      const int st = sm.before[e], ce = sm.after[e];
+      const int end = st + (ce + bm - 1) / bm * bm;
+      for (int p = st + ce + lane; p < end; p += kWave) sorted_ids[p] = M;
+      for (int b = st / bm + lane; b < end / bm; b += kWave) block_expert[b] = e;
+    }
+  }
+
+  // 4. each wave places its own routes in order; only wave-private LDS is used
   static_assert(kMaxExperts <= 1023, "expert key needs more bits");
   const unsigned long long below = (1ull << lane) - 1;
   auto local_id = [&](int f) {
