@@ -145,6 +145,33 @@ def test_tile_kernel_short_and_odd_k(H, I, E, k, M):
     check_forward(layer, hidden, ids, wts, host_bf16_bits(out), xd, idd)
 
 
+@pytest.mark.parametrize("M", [40, 2100, 4000])
+def test_forward_most_experts_and_slots(M):
+    """The largest expert count (512) and top-k (8) the library takes, at
+    blocks of 16, 64 and 128 routes (mean routes per expert 0.6, 33, 63),
+    every token against the oracle."""
+    base = wl.WORKLOADS["backbone-decode"]
+    w = wl.scaled(base, hidden=512, inter=128, inter_valid=128, num_experts=512, routed_experts=512, topk=8,
+                  config_id=500)
+    layer = Layer(w)
+    hidden, ids, wts = wl.make_inputs(w, M, "softmax")
+    d = layer.dims(M)
+    bm = abi.moe_a8w4_block_m(d)
+    note("most experts and slots M=%d bm=%d" % (M, bm))
+    out = torch.full((M, w.hidden), float("nan"), dtype=torch.bfloat16, device=DEV)
+    xd, idd = dev(hidden), dev(ids)
+    layer.forward(xd, idd, wts, out=out)
+    torch.cuda.synchronize()
+    srt, bexp, npad = abi.moe_a8w4_sort(d, bm, idd)
+    torch.cuda.synchronize()
+    ref_sorted, ref_bexp = oracle.sort(ids, w.num_experts, w.expert_offset, bm)
+    P = int(npad.item())
+    assert P == len(ref_sorted)
+    assert np.array_equal(srt[:P].cpu().numpy(), ref_sorted)
+    assert np.array_equal(bexp[:P // bm].cpu().numpy(), ref_bexp)
+    check_forward(layer, hidden, ids, wts, host_bf16_bits(out), xd, idd)
+
+
 def test_edge_cases():
     w = wl.scaled(wl.WORKLOADS["backbone-decode"], num_experts=12, routed_experts=12, config_id=120)
     layer = Layer(w)
