@@ -207,8 +207,9 @@ int moe_a8w4_sort(const moe_a8w4_dims* dims, int32_t block_m, const int32_t* top
                   hipStream_t stream);
 
 /* moe_a8w4_quant_act and moe_a8w4_sort of one call in a single launch (the
- * sort runs in one workgroup beside the quantiser): the first step of
- * moe_a8w4_forward.  Same buffers and contracts as the two calls. */
+ * sort's workgroups, one per 1024 routes up to 64, run beside the
+ * quantiser's): the first step of moe_a8w4_forward.  Same buffers and
+ * contracts as the two calls. */
 int moe_a8w4_quant_sort(const moe_a8w4_dims* dims, int32_t block_m, const void* hidden,
                         const int32_t* topk_ids, uint8_t* a_q, uint8_t* a_s, int32_t* sorted_ids,
                         int32_t* block_expert, int32_t* num_padded, hipStream_t stream);
