@@ -639,16 +639,21 @@ static_assert(MOE_TILE_STAGES >= 3, "the stage-two epilogue borrows the two ring
 
 // Slices per workgroup of the token-resident kernel for this launch (0: not
 // used): the token tile must fit; of the group sizes that split the 256-row
-// slices evenly, the largest that still leaves two workgroups per CU (at
-// prefill-shared M=16384 stage two: 4 slices 749 us, 10 slices 690 us, 20
-// slices 762 us, too few workgroups), else the smallest.
+// slices evenly, the largest that still leaves eight workgroups per CU for the
+// routing-free bound on the tiles (max_tiles), else the smallest.  One
+// workgroup fits a CU at a time, so fewer, longer workgroups leave a larger
+// last round.  Measured (stage two, us): prefill-shared 2048 tokens 10 slices
+// 178, 5 slices 170; 4096 tokens 229 / 210; 8192 tokens 261 / 251; 16384
+// tokens keeps 10 (4 slices 749 against 690 in an earlier version, 20 slices
+// 762); at the backbone geometry's 2048 and 4096 tokens, where the blocks
+// fill whole rounds, 5 slices cost 2-6 us more.
 int resident_slices(const GemmArgs& a, int64_t max_tiles) {
   if ((int64_t)a.bm * a.K > kResidentBytes) return 0;
   const int slices = a.N / 256;
   int pick = 0;
   for (int ns : {4, 5, 10}) {
     if (slices % ns) continue;
-    if (pick == 0 || max_tiles / ns >= 512) pick = ns;
+    if (pick == 0 || max_tiles / ns >= 2048) pick = ns;
   }
   return pick;
 }
