@@ -40,14 +40,29 @@ int status_of(hipError_t e) { return e == hipSuccess ? MOE_OK : (int)e; }
 
 bool valid_bm(int bm) { return bm == 16 || bm == 32 || bm == 64 || bm == 128; }
 
-// Rows per sorted block from the mean number of routes per expert (for a
-// local slice of experts, over all the experts the router chooses among).
+// Mean routes per routed expert, the statistic the block size follows.  For
+// a local slice of experts the router's routes spread over all the experts
+// it chooses among (routed_experts > num_experts).  A layer that holds more
+// experts than the router chooses among (routed_experts < num_experts) holds
+// num_experts - routed_experts shared experts, each taking one of every
+// token's top-k slots; those routes fill the shared experts' own blocks and
+// are left out of the mean.
+double routes_per_expert(const moe_a8w4_dims* d) {
+  if (d->routed_experts > 0 && d->routed_experts < d->num_experts) {
+    const int shared = d->num_experts - d->routed_experts;
+    const int k = d->topk > shared ? d->topk - shared : d->topk;
+    return (double)d->tokens * k / d->routed_experts;
+  }
+  const int experts = d->routed_experts > d->num_experts ? d->routed_experts : d->num_experts;
+  return (double)d->tokens * d->topk / experts;
+}
+
+// Rows per sorted block from the mean number of routes per routed expert.
 // Column groups of 16 past a block's last route are skipped by the GEMMs, so
 // a larger block only costs padding; a smaller one re-reads an expert's
 // weights once per extra block.
 int choose_bm(const moe_a8w4_dims* d) {
-  const int experts = d->routed_experts > d->num_experts ? d->routed_experts : d->num_experts;
-  const double avg = (double)d->tokens * d->topk / experts;
+  const double avg = routes_per_expert(d);
   if (avg <= 8.0) return 16;
   if (avg <= 20.0) return 32;   // local slice: 16 per expert, 32 beat 64 by 9 %; 24, 64 beat 32 by 8 %
   if (avg <= 40.0) return 64;
@@ -146,8 +161,7 @@ moe::FusedArgs fused_args(const moe_a8w4_dims* d, int bm, int32_t* cnt, const in
 // blocks of 64 beat 32 (759 against 818); 16384 tokens: 2851 us in blocks of
 // 64, 2515 in blocks of 128.
 int a16_bm(const moe_a8w4_dims* d) {
-  const int experts = d->routed_experts > d->num_experts ? d->routed_experts : d->num_experts;
-  const double avg = (double)d->tokens * d->topk / experts;
+  const double avg = routes_per_expert(d);
   return avg <= 8.0 ? 16 : avg <= 40.0 ? 32 : avg <= 64.0 ? 64 : 128;
 }
 

@@ -94,6 +94,15 @@ def test_block_m_capacity_and_workspace_sizes():
     assert abi.moe_a8w4_block_m(dims(tokens=336, num_experts=96, topk=6)) == 64    # 21
     d.routed_experts = -1
     assert abi.load().moe_a8w4_block_m(ctypes.byref(d)) == abi.MOE_ERR_DIMS
+    # 385 experts of which the router chooses among 384: one shared expert in
+    # one of the 7 slots, so the routed experts get M * 6 / 384 routes each
+    d = dims(tokens=2560, num_experts=385, topk=7)
+    d.routed_experts = 384
+    assert abi.moe_a8w4_block_m(d) == 64          # 40 per routed expert (46.5 counting the shared slot)
+    d = dims(tokens=4096, num_experts=385, topk=7, inter=768)
+    d.routed_experts = 384
+    assert abi.moe_a16w4_block_m(d) == 64         # 64 per routed expert (74.5 counting the shared slot)
+    assert abi.moe_a8w4_block_m(d) == 128
     d = dims(tokens=33, num_experts=384, topk=6)
     R = 33 * 6
     for bm in (16, 32, 64, 128):
