@@ -19,9 +19,10 @@ per-bucket microseconds / GB/s / TFLOP/s, the roofline position of the
 dominant kernel (stage one, timed with HIP events on its stream inside the
 timed loop), the CPU oracle timed on every bucket as a baseline, and -- the
 MFMA-bound half of the metric -- a prefill block: the prefill geometry with
-the fused shared expert (385 experts, top-7) at 4096 and 16384 tokens and the
-local-slice geometry (96 of 384 experts, I 2304) at 16384 tokens, each call
-after a cache-evicting write, with the stage-one tile kernel's roofline.
+the fused shared expert (385 experts, top-7) at 4096 and 16384 tokens
+(round-robin, and softmax at 16384) and the local-slice geometry (96 of 384
+experts, I 2304) at 16384 tokens, each call after an untimed 1 GiB read that
+evicts the caches, with the stage-one tile kernel's roofline.
 """
 from __future__ import annotations
 
