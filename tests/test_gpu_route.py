@@ -23,7 +23,8 @@ def check_route(logits, k_routed, shared, ids, wts):
 
 @pytest.mark.parametrize("M,Er,kr,shared", [(64, 384, 6, -1), (33, 128, 3, -1), (40, 384, 6, 384),
                                            (17, 100, 8, -1), (5, 8, 1, 7), (3000, 384, 6, -1),
-                                           (9, 512, 7, 512)])
+                                           (9, 512, 7, 512),
+                                           (16384, 384, 6, 384)])   # the prefill geometry's full call
 def test_route_matches_oracle(M, Er, kr, shared):
     rng = np.random.default_rng(M * 7 + Er)
     logits = rng.standard_normal((M, Er), dtype=np.float32)
